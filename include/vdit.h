@@ -1,0 +1,227 @@
+/*
+ * vdit.h - C ABI of the MI355X (gfx950) RoPE3D + block-sparse KV-cache attention library.
+ *
+ * One attention call of a video diffusion transformer's denoising chunk: the chunk's
+ * queries, rotated by a 3D rotary encoding whose time coordinate is the global frame
+ * index (start frame t0 + local frame), attend to a ring-buffer KV cache of earlier
+ * frames under a chunk-causal, log-radial or dense visibility rule, computed as a
+ * tiled flash-attention forward pass that never touches invisible key tiles.
+ *
+ * Conventions for every entry point
+ * - Return value: VDIT_OK (0) or a VDIT_ERR_* status.  All arguments are validated
+ *   before anything is enqueued: on error nothing was launched and no output was
+ *   touched.  vdit_last_error() returns a message for the calling thread's last error.
+ *   Faults inside a kernel surface at the caller's next synchronisation; a launch the
+ *   runtime rejects returns VDIT_ERR_DEVICE.
+ * - Memory: every buffer is allocated and owned by the caller.  Pointers documented
+ *   "device" must be device memory of the current HIP device, "host" plain host memory.
+ *   The library allocates no device memory and keeps no global state besides the
+ *   per-thread error string.
+ * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
+ *   work is only enqueued; no call synchronises the device.
+ * - Tensors [tokens][heads][channels]: vdit_tensor gives the base pointer, dtype and the
+ *   token / head strides in ELEMENTS; channels are contiguous.  Base pointers must be
+ *   16-byte aligned and strides multiples of 8 (bf16) or 4 (fp32) elements.
+ * - Token order inside a call: frame-major, then row h, then column w.
+ */
+#ifndef VDIT_H
+#define VDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDIT_ABI_VERSION 1
+
+/* status codes */
+#define VDIT_OK 0
+#define VDIT_ERR_INVALID_ARG 1
+#define VDIT_ERR_BUFFER_TOO_SMALL 2
+#define VDIT_ERR_UNSUPPORTED 3
+#define VDIT_ERR_DEVICE 4
+
+/* element types of Q / K / V / O */
+#define VDIT_DTYPE_BF16 0
+#define VDIT_DTYPE_FP32 1
+
+/* visibility rules */
+#define VDIT_MASK_DENSE 0
+#define VDIT_MASK_CHUNK_CAUSAL 1
+#define VDIT_MASK_LOG_RADIAL 2
+
+/* where a plan or position list is produced */
+#define VDIT_WHERE_HOST 0
+#define VDIT_WHERE_DEVICE 1
+
+/* plan word layout (int32): header, then query tiles, row pointers and spans */
+#define VDIT_PLAN_MAGIC 0x54494456 /* 'V' 'D' 'I' 'T' */
+#define VDIT_PLAN_VERSION 1
+#define VDIT_PLAN_HEADER_WORDS 8
+
+typedef struct {
+    void* data;           /* device */
+    int32_t dtype;        /* VDIT_DTYPE_* */
+    int32_t reserved;     /* must be 0 */
+    int64_t stride_token; /* elements between consecutive tokens */
+    int64_t stride_head;  /* elements between consecutive heads */
+} vdit_tensor;
+
+typedef struct {
+    int32_t frames, height, width; /* latent frames of height x width tokens */
+} vdit_grid;
+
+/* 3D rotary encoding.  Channels are split [t | h | w] with widths dim_t, dim_h, dim_w
+ * (each even, summing to head_dim).  Pair (2j, 2j+1) of an axis group of width d is
+ * rotated by p * theta^(-2j/d), p being the token's coordinate on that axis. */
+typedef struct {
+    int32_t head_dim, dim_t, dim_h, dim_w;
+    double theta;
+    int32_t max_t, max_h, max_w; /* table rows per axis: t < max_t, h < max_h, w < max_w */
+    int32_t reserved;            /* must be 0 */
+    const float* table;          /* device copy of vdit_rope_table_build's output (may be
+                                    NULL for vdit_rope_table_build itself) */
+} vdit_rope_cfg;
+
+/* Ring-buffer KV cache of `capacity` frames of tokens_per_frame tokens.  Frame t lives in
+ * slot t mod capacity.  Slot pitch frame_stride = tokens_per_frame rounded up to 8;
+ * the physical key index of token s of slot j is j * frame_stride + s, and
+ * kv_rows = capacity * frame_stride.
+ *   k: device bf16 [heads][kv_rows][head_dim], keys already rotated at their global
+ *      position;
+ *   v: device bf16 [heads][head_dim][kv_rows] (values stored transposed, keys contiguous);
+ *   slot_frame_dev / slot_frame_host: int32 [capacity], the global frame held by each
+ *      slot or -1; the host array mirrors the device array and is updated synchronously
+ *      by vdit_kv_append. */
+typedef struct {
+    void* k;
+    void* v;
+    int32_t* slot_frame_dev;
+    int32_t* slot_frame_host;
+    int32_t capacity, tokens_per_frame, heads, head_dim;
+} vdit_kv_cache;
+
+/* Visibility rule.  tile = 128 (query and key tile length of the plan).
+ * CHUNK_CAUSAL: query at global frame tq sees key frame tk iff
+ *   floor(tk / chunk_frames) <= floor(tq / chunk_frames).
+ * LOG_RADIAL: with d = |tq - tk| and spatial tile indices (within-frame index / tile),
+ *   a key is visible iff d == 0, or long_range_period > 0 and d % long_range_period == 0,
+ *   or |tile_q - tile_k| <= W(d) = ceil(radial_w0 * 2^(-radial_decay_log2 * d)). */
+typedef struct {
+    int32_t kind;
+    int32_t chunk_frames;
+    int32_t tile;
+    int32_t radial_w0;
+    int32_t radial_decay_log2;
+    int32_t long_range_period;
+} vdit_mask_cfg;
+
+/* ---- informational -------------------------------------------------------------- */
+int vdit_abi_version(void);
+const char* vdit_last_error(void);
+const char* vdit_status_string(int status);
+
+/* ---- positions: "Accelerating Video Generation Inference with Sequential-Parallel 3D
+ * Positional Encoding Using a Global Time Index", section 2.B (Causal-RoPE SP): a token's
+ * global time index is its local frame plus the block's start frame.
+ * Writes int32 [frames*height*width][3] = (t0 + f, h, w).  where = VDIT_WHERE_HOST: `out`
+ * is host memory, filled before return (stream ignored); VDIT_WHERE_DEVICE: `out` is
+ * device memory, written by a kernel on `stream`.  Errors: negative sizes or t0,
+ * NULL out -> INVALID_ARG. */
+int vdit_token_positions(vdit_grid grid, int32_t t0, int32_t where, int32_t* out, void* stream);
+
+/* ---- RoPE tables: same page, section 2.C ("Pre-calculo do RoPE"): frequencies are
+ * precomputed once into contiguous tensors instead of a dynamic cache.
+ * Number of floats of the table: max_t*dim_t + max_h*dim_h + max_w*dim_w.
+ * Layout: per axis in the order t, h, w, [rows][dim_a/2] pairs of (cos, sin) as float,
+ * computed in double precision on the host and rounded to float.
+ * host_out is host memory; the caller copies it to the device and stores the device
+ * pointer in cfg->table.  Errors: odd or negative widths, widths not summing to
+ * head_dim, theta <= 0, non-positive table rows -> INVALID_ARG; cap_floats too small
+ * -> BUFFER_TOO_SMALL (*needed_floats is still set). */
+int vdit_rope_table_build(const vdit_rope_cfg* cfg, float* host_out, size_t cap_floats,
+                          size_t* needed_floats);
+
+/* ---- RoPE3D in place: "Timeripple: Accelerating vDiTs by Understanding the
+ * Spatio-Temporal Correlations in Latent Space", Metodologia 1 (RoPE channel groups
+ * for time and the two spatial axes) with the global time index above.
+ * Rotates q and/or k ([frames*height*width][heads][head_dim], bf16 or fp32, device) in
+ * place at positions (t0 + f, h, w); fp32 arithmetic, one rounding to the tensor's
+ * dtype.  A tensor with data == NULL is skipped.  Errors: coordinates beyond the table
+ * rows, head_dim not 64 or 128, bad strides -> INVALID_ARG / UNSUPPORTED. */
+int vdit_rope3d_qk(const vdit_rope_cfg* cfg, vdit_grid grid, int32_t t0, int32_t heads,
+                   vdit_tensor q, vdit_tensor k, void* stream);
+
+/* ---- KV cache: "Accelerating Video Generation Inference ...", section 2.A (KV cache of
+ * causal chunk inference) and the Wave Forcing / WaveRT page (cache refresh once a
+ * block is denoised).
+ * vdit_kv_cache_bytes: sizes of the caller-allocated k and v buffers.
+ * vdit_kv_cache_reset: marks every slot empty (-1) in both slot tables; the device table
+ *   is written by a kernel on `stream`. */
+int vdit_kv_cache_bytes(int32_t capacity, int32_t tokens_per_frame, int32_t heads, int32_t head_dim,
+                        size_t* k_bytes, size_t* v_bytes);
+int vdit_kv_cache_reset(vdit_kv_cache* cache, void* stream);
+
+/* vdit_kv_append: writes `grid.frames` frames starting at global frame t0.  Frame t0+f
+ * goes to slot (t0+f) mod capacity, evicting what the slot held.  k and v are
+ * [frames*tokens_per_frame][heads][head_dim] (bf16 or fp32, device).  If rope is not NULL
+ * the keys are rotated at their global positions (t0+f, h, w) before the write (fp32
+ * arithmetic, one rounding to bf16); with rope == NULL they are stored as given.  Values
+ * are rounded to bf16 and stored transposed.  The padding tokens of each written slot
+ * (tokens_per_frame .. frame_stride-1) are zeroed.  Both slot tables are updated (the host
+ * one before return).  Errors: grid.height*grid.width != tokens_per_frame, frames < 1 or
+ * > capacity, t0 < 0, coordinates beyond the rope table, shape mismatch -> INVALID_ARG. */
+int vdit_kv_append(vdit_kv_cache* cache, const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0,
+                   vdit_tensor k, vdit_tensor v, void* stream);
+
+/* ---- block plan: Wave Forcing / WaveRT page (block-causal attention);
+ * "DynamicRad: Content-Adaptive Sparse Attention for Long Video Diffusion", section 2
+ * (log-radial window, long-range factor, static-ratio mode).
+ * The query rows of a call are cut into query tiles: consecutive `tile`-row pieces of
+ * each mask unit (the whole call for DENSE, the call frames of one causal chunk for
+ * CHUNK_CAUSAL, one frame for LOG_RADIAL), so that all rows of a tile see the same keys.
+ * For every tile the plan lists the maximal ascending runs ("spans") of visible physical
+ * key indices of the cache's occupied slots.
+ * Words (int32): header[8] = {VDIT_PLAN_MAGIC, VDIT_PLAN_VERSION, kind, tile, n_qtiles,
+ * n_spans, pairs_lo, pairs_hi} where pairs = sum over tiles of q_len * (sum of span
+ * lengths); then {q_start, q_len}[n_qtiles]; row_ptr[n_qtiles + 1]; {k_start, k_len}[n_spans].
+ * vdit_plan_qtiles: number of query tiles (depends on the rule and grid only).
+ * vdit_plan_bound: upper bound on the plan size in words for this cache.
+ * vdit_plan_mask: where = VDIT_WHERE_HOST reads slot_frame_host and writes host memory
+ *   before return (*used_words = exact size); VDIT_WHERE_DEVICE reads slot_frame_dev and
+ *   writes device memory from a kernel on `stream` (*used_words = the bound).  Host and
+ *   device plans are identical word for word.  Errors: grid tokens per frame differing
+ *   from the cache's, tile != 128, chunk_frames < 1, radial parameters < 0 -> INVALID_ARG;
+ *   cap_words below the bound -> BUFFER_TOO_SMALL. */
+int vdit_plan_qtiles(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, int32_t* n_qtiles);
+int vdit_plan_bound(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
+                    size_t* max_words);
+int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
+                   int32_t where, int32_t* plan_out, size_t cap_words, size_t* used_words, void* stream);
+
+/* ---- attention forward: the full spatiotemporal softmax attention of "DynamicRad ..."
+ * section 1 and "Accelerating Video Generation Inference ..." section 1, restricted to
+ * the visible keys of the plan, as a tiled (FlashAttention-style) pass that skips the
+ * invisible tiles.
+ * q: [frames*height*width][heads][head_dim] bf16 or fp32 (device); if rope != NULL the
+ *   queries are rotated at (q_t0 + f, h, w) while they are loaded (fp32 arithmetic, one
+ *   rounding to bf16); with rope == NULL they are used as given (rounded to bf16).
+ * plan_dev: device plan built for this rule, grid, q_t0 and the cache's current slots.
+ * softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * o: same shape as q, bf16 or fp32 (device).  lse: NULL or device fp32 [heads][tokens],
+ *   natural-log log-sum-exp of each row's scaled logits (-inf for a row with no visible
+ *   key, whose output is 0).
+ * Arithmetic: bf16 products with fp32 accumulation, fp32 online softmax, P rounded to
+ * bf16 before the P.V product.  Errors: head counts or head_dim differing from the
+ * cache's, head_dim not 64 or 128 -> INVALID_ARG / UNSUPPORTED. */
+int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
+                        const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
+                        float softmax_scale, vdit_tensor o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDIT_H */

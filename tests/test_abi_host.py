@@ -1,0 +1,229 @@
+"""Host-side checks of libvdit: symbols, host plan builder, RoPE tables, positions, errors.
+
+No GPU is needed: these calls never launch a kernel (host plan and positions are built on
+the host; every error is detected before any launch).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, get_workload
+from video_diffusion_transformer_rope3d_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    header = open(os.path.join(ROOT, "include", "vdit.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(vdit_\w+)\s*\(", header, re.M))
+    assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name)
+    assert B.vdit_abi_version() == 1
+    assert B.vdit_status_string(2) == "buffer too small"
+
+
+def host_cache(w, slot_table):
+    """Cache descriptor with only the host slot table (what the host plan builder reads)."""
+    st = np.ascontiguousarray(slot_table, dtype=np.int32)
+    desc = B.VditKVCache(None, None, None, st.ctypes.data, w.capacity, w.tokens_per_frame, w.heads, w.head_dim)
+    return desc, st
+
+
+def host_plan(w, desc):
+    m = w.mask
+    mask = B.mask_cfg(m.kind, m.chunk_frames, m.tile, m.radial_w0, m.radial_decay_log2, m.long_range_period)
+    g = B.grid(w.q_frames, w.frame_h, w.frame_w)
+    bound = ctypes.c_size_t(0)
+    assert B.lib().vdit_plan_bound(ctypes.byref(mask), g, w.q_t0, ctypes.byref(desc), ctypes.byref(bound)) == 0
+    buf = np.zeros(bound.value, np.int32)
+    used = ctypes.c_size_t(0)
+    st = B.lib().vdit_plan_mask(ctypes.byref(mask), g, w.q_t0, ctypes.byref(desc), B.VDIT_WHERE_HOST,
+                                buf.ctypes.data, buf.size, ctypes.byref(used), None)
+    assert st == 0, B.vdit_last_error()
+    return buf[:used.value]
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if n != "log_radial"])
+def test_host_plan_bit_exact_vs_oracle(name):
+    w = get_workload(name)
+    st = oracle.build_layout(w)
+    desc, keep = host_cache(w, st.ring.slot_frame)
+    got = host_plan(w, desc)
+    want = oracle.plan_for(st)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.slow
+def test_host_plan_bit_exact_vs_oracle_log_radial():
+    w = get_workload("log_radial")
+    st = oracle.build_layout(w)
+    desc, keep = host_cache(w, st.ring.slot_frame)
+    np.testing.assert_array_equal(host_plan(w, desc), oracle.plan_for(st))
+
+
+def test_host_plan_random_small_grids():
+    """Random rules, grids, start frames and partly filled / wrapped rings."""
+    from workloads.configs import MaskSpec, Workload
+    rng = np.random.default_rng(123)
+    for trial in range(40):
+        kind = ["dense", "chunk_causal", "log_radial"][trial % 3]
+        fh, fw = int(rng.integers(1, 14)), int(rng.integers(1, 30))
+        cap = int(rng.integers(1, 9))
+        frames = int(rng.integers(1, cap + 1))
+        t0 = int(rng.integers(0, 40))
+        mask = MaskSpec(kind, chunk_frames=int(rng.integers(1, 5)), radial_w0=int(rng.integers(0, 6)),
+                        radial_decay_log2=int(rng.integers(0, 3)), long_range_period=int(rng.integers(0, 4)))
+        hist = []
+        t = max(0, t0 - int(rng.integers(0, 3 * cap)))
+        while t < t0:
+            f = min(int(rng.integers(1, cap + 1)), t0 - t)
+            hist.append((t, f))
+            t += f
+        w = Workload(name="rand", description="", heads=1, head_dim=64, frame_h=fh, frame_w=fw, q_frames=frames,
+                     q_t0=t0, rope_dims=(24, 20, 20), theta=1e4, mask=mask, capacity=cap, history=tuple(hist))
+        st = oracle.build_layout(w)
+        desc, keep = host_cache(w, st.ring.slot_frame)
+        np.testing.assert_array_equal(host_plan(w, desc), oracle.plan_for(st), err_msg=str(w))
+
+
+def test_plan_qtiles_and_bound():
+    w = get_workload("wan13b_chunk")
+    mask = B.mask_cfg("chunk_causal", 3)
+    assert B.vdit_plan_qtiles(mask, B.grid(3, 30, 52), 6) == 37
+    assert B.vdit_plan_qtiles(B.mask_cfg("log_radial"), B.grid(21, 30, 52), 0) == 273
+    assert B.vdit_plan_qtiles(B.mask_cfg("dense"), B.grid(21, 30, 52), 0) == 256
+    # a call straddling a chunk boundary is cut at the boundary
+    assert B.vdit_plan_qtiles(mask, B.grid(3, 30, 52), 400) == 25 + 13
+
+
+def test_positions_host_bit_exact():
+    for (f, hgt, wid, t0) in [(3, 4, 6, 5), (3, 30, 52, 396), (1, 1, 1, 0), (2, 10, 13, 7)]:
+        got = B.vdit_token_positions(B.grid(f, hgt, wid), t0, B.VDIT_WHERE_HOST)
+        np.testing.assert_array_equal(got, oracle.token_positions(f, hgt, wid, t0).astype(np.int32))
+
+
+def test_rope_table_matches_oracle_angles():
+    cfg = B.rope_cfg(128, (44, 42, 42), 1e4, 402, 30, 52)
+    tab = B.vdit_rope_table_build(cfg)
+    assert tab.size == 402 * 44 + 30 * 42 + 52 * 42
+    off = 0
+    for d_a, rows in ((44, 402), (42, 30), (42, 52)):
+        ang = np.arange(rows)[:, None] * oracle.axis_frequencies(d_a, 1e4)[None, :]
+        part = tab[off:off + rows * d_a].reshape(rows, d_a // 2, 2)
+        np.testing.assert_allclose(part[..., 0], np.cos(ang), atol=6e-8, rtol=0)
+        np.testing.assert_allclose(part[..., 1], np.sin(ang), atol=6e-8, rtol=0)
+        off += rows * d_a
+
+
+# ------------------------------------------------------------------ error paths
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_rope_table_errors(L):
+    need = ctypes.c_size_t(0)
+    for dims, hd in [((23, 21, 20), 64), ((24, 20, 22), 64), ((22, 21, 21), 64)]:
+        cfg = B.rope_cfg(hd, dims, 1e4, 8, 4, 6)
+        assert L.vdit_rope_table_build(ctypes.byref(cfg), None, 0, ctypes.byref(need)) == B.VDIT_ERR_INVALID_ARG
+        assert "rope" in B.vdit_last_error()
+    cfg = B.rope_cfg(64, (24, 20, 20), 1e4, 8, 4, 6)
+    small = np.zeros(10, np.float32)
+    assert L.vdit_rope_table_build(ctypes.byref(cfg), small.ctypes.data, small.size,
+                                   ctypes.byref(need)) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    assert need.value == 8 * 24 + 4 * 20 + 6 * 20
+    bad = B.rope_cfg(64, (24, 20, 20), -1.0, 8, 4, 6)
+    assert L.vdit_rope_table_build(ctypes.byref(bad), None, 0, ctypes.byref(need)) == B.VDIT_ERR_INVALID_ARG
+
+
+def test_plan_errors(L):
+    w = get_workload("tiny")
+    st = oracle.build_layout(w)
+    desc, keep = host_cache(w, st.ring.slot_frame)
+    g = B.grid(3, 4, 6)
+    used = ctypes.c_size_t(0)
+    buf = np.zeros(4, np.int32)
+    m = B.mask_cfg("chunk_causal", 1)
+    assert L.vdit_plan_mask(ctypes.byref(m), g, 5, ctypes.byref(desc), B.VDIT_WHERE_HOST, buf.ctypes.data, buf.size,
+                            ctypes.byref(used), None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    assert used.value == 8 + 3 * 3 + 1 + 2 * 4  # exact size is reported
+    assert (buf == 0).all()  # nothing written
+    big = np.zeros(256, np.int32)
+    for bad_mask, code in [(B.mask_cfg("chunk_causal", 0), B.VDIT_ERR_INVALID_ARG),
+                           (B.mask_cfg("chunk_causal", 1, tile=64), B.VDIT_ERR_UNSUPPORTED),
+                           (B.mask_cfg(7), B.VDIT_ERR_INVALID_ARG),
+                           (B.mask_cfg("log_radial", radial_w0=-1), B.VDIT_ERR_INVALID_ARG)]:
+        assert L.vdit_plan_mask(ctypes.byref(bad_mask), g, 5, ctypes.byref(desc), B.VDIT_WHERE_HOST,
+                                big.ctypes.data, big.size, ctypes.byref(used), None) == code
+    # grid that does not match the cache's frame size
+    assert L.vdit_plan_mask(ctypes.byref(m), B.grid(3, 4, 7), 5, ctypes.byref(desc), B.VDIT_WHERE_HOST,
+                            big.ctypes.data, big.size, ctypes.byref(used), None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_plan_mask(ctypes.byref(m), g, -1, ctypes.byref(desc), B.VDIT_WHERE_HOST,
+                            big.ctypes.data, big.size, ctypes.byref(used), None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_plan_mask(ctypes.byref(m), g, 5, None, B.VDIT_WHERE_HOST,
+                            big.ctypes.data, big.size, ctypes.byref(used), None) == B.VDIT_ERR_INVALID_ARG
+
+
+def test_cache_and_append_errors(L):
+    kb, vb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.vdit_kv_cache_bytes(21, 1560, 12, 128, ctypes.byref(kb), ctypes.byref(vb)) == 0
+    assert kb.value == vb.value == 12 * 21 * 1560 * 128 * 2
+    assert L.vdit_kv_cache_bytes(3, 130, 2, 128, ctypes.byref(kb), ctypes.byref(vb)) == 0
+    assert kb.value == 2 * 3 * 136 * 128 * 2  # slot pitch rounded up to 8 tokens
+    assert L.vdit_kv_cache_bytes(21, 1560, 12, 96, ctypes.byref(kb), ctypes.byref(vb)) == B.VDIT_ERR_UNSUPPORTED
+    assert L.vdit_kv_cache_bytes(0, 1560, 12, 128, ctypes.byref(kb), ctypes.byref(vb)) == B.VDIT_ERR_INVALID_ARG
+    slots = np.full(3, -1, np.int32)
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+    desc = B.VditKVCache(fake, fake, fake, slots.ctypes.data, 3, 24, 2, 64)
+    t = B.VditTensor(0x10000, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    # frames beyond capacity, grid mismatch, negative t0, null tensor, bad dtype
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(4, 4, 6), 0, t, t, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(1, 5, 6), 0, t, t, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(1, 4, 6), -2, t, t, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(1, 4, 6), 0, B.VditTensor(None, 0, 0, 128, 64), t,
+                            None) == B.VDIT_ERR_INVALID_ARG
+    bad_dt = B.VditTensor(0x10000, 5, 0, 128, 64)
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(1, 4, 6), 0, bad_dt, t, None) == B.VDIT_ERR_UNSUPPORTED
+    misaligned = B.VditTensor(0x10002, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(1, 4, 6), 0, misaligned, t,
+                            None) == B.VDIT_ERR_INVALID_ARG
+    mixed = B.VditTensor(0x10000, B.VDIT_DTYPE_FP32, 0, 128, 64)
+    assert L.vdit_kv_append(ctypes.byref(desc), None, B.grid(1, 4, 6), 0, t, mixed, None) == B.VDIT_ERR_INVALID_ARG
+    # rope table too short for the global frames of the append
+    rope = B.rope_cfg(64, (24, 20, 20), 1e4, 3, 4, 6)
+    rope.table = 0x10000
+    assert L.vdit_kv_append(ctypes.byref(desc), ctypes.byref(rope), B.grid(1, 4, 6), 3, t, t,
+                            None) == B.VDIT_ERR_INVALID_ARG
+    assert slots.tolist() == [-1, -1, -1]  # failed appends leave the slot table alone
+
+
+def test_attention_errors(L):
+    slots = np.array([0, 1, 2], np.int32)
+    fake = 0x10000
+    desc = B.VditKVCache(fake, fake, fake, slots.ctypes.data, 3, 24, 2, 64)
+    m = B.mask_cfg("chunk_causal", 1)
+    t = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    g = B.grid(3, 4, 6)
+    # null plan, null output, grid mismatch, bad scale is fine (defaults) but head mismatch is not
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(m), None, 0.0, t, None,
+                                 None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0,
+                                 B.VditTensor(None, 0, 0, 128, 64), None, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_attn_fwd(t, None, B.grid(3, 4, 5), 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
+                                 None, None) == B.VDIT_ERR_INVALID_ARG
+    narrow = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 64, 32)  # head stride below head_dim
+    assert L.vdit_block_attn_fwd(narrow, None, g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t, None,
+                                 None) == B.VDIT_ERR_INVALID_ARG
+    rope = B.rope_cfg(128, (44, 42, 42), 1e4, 16, 4, 6)  # head_dim differs from the cache's
+    rope.table = fake
+    assert L.vdit_block_attn_fwd(t, ctypes.byref(rope), g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
+                                 None, None) == B.VDIT_ERR_INVALID_ARG

@@ -1,0 +1,198 @@
+"""GPU parity of libvdit against the fp64 oracle, through the C ABI.
+
+Bars: positions, slot tables and plans bit-exact; attention outputs within max-abs 2e-2 and
+relative L2 5e-3 (bf16 inputs, fp32 accumulation); full outputs for the reduced workloads,
+sampled rows (tile edges, ragged tails, random rows) of sampled heads for the full-size ones,
+which run in the same launch configuration as the benchmark.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import get_workload, make_inputs
+from video_diffusion_transformer_rope3d_amd import binding as B
+
+from harness import compare, device_plan_words, run_workload, sample_rows, session_for, to_dev, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "tiny_d128", "small_chunk_pad", "small_radial", "small_dense_d64", "wan13b_chunk_h2"]
+LARGE = ["wan13b_chunk", "stream_wrap_straddle", "log_radial", "dense_clip", "stream14b_chunk"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ integer parts
+def test_positions_device_bit_exact():
+    for (f, hgt, wid, t0) in [(3, 4, 6, 5), (3, 30, 52, 396), (21, 30, 52, 0), (2, 10, 13, 401)]:
+        got = B.vdit_token_positions(B.grid(f, hgt, wid), t0, B.VDIT_WHERE_DEVICE).cpu().numpy()
+        np.testing.assert_array_equal(got, oracle.token_positions(f, hgt, wid, t0).astype(np.int32))
+
+
+@pytest.mark.parametrize("name", SMALL + LARGE)
+def test_device_plan_bit_exact(name):
+    _print("device plan", name)
+    w = get_workload(name)
+    s = session_for(w)
+    dt = torch_dtype(w)
+    hw = w.tokens_per_frame
+    for t0, f in w.appends():  # slot tables only matter: append zeros
+        z = torch.zeros((f * hw, w.heads, w.head_dim), dtype=dt, device="cuda")
+        s.append(z, z, t0)
+    st = oracle.build_layout(w)
+    np.testing.assert_array_equal(s.cache.slot_dev.cpu().numpy(), st.ring.slot_frame)
+    np.testing.assert_array_equal(s.cache.slot_host, st.ring.slot_frame)
+    want = oracle.plan_for(st) if name != "log_radial" else None
+    dev = device_plan_words(s.plan(w.q_frames, w.q_t0, B.VDIT_WHERE_DEVICE))
+    host = s.plan(w.q_frames, w.q_t0, B.VDIT_WHERE_HOST)
+    np.testing.assert_array_equal(dev, host)
+    if want is not None:
+        np.testing.assert_array_equal(dev, want)
+
+
+# ------------------------------------------------------------------ RoPE and the cache
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rope_inplace_vs_oracle(dtype):
+    rng = np.random.default_rng(7)
+    fr, hgt, wid, t0, heads = 3, 30, 52, 396, 3
+    x = rng.standard_normal((fr * hgt * wid, heads, 128)).astype(np.float32)
+    xd = to_dev(x, dtype)
+    exact = xd.float().cpu().numpy().astype(np.float64)  # the values the kernel starts from
+    rope = B.Rope(128, (44, 42, 42), 1e4, 400, 30, 52)
+    B.vdit_rope3d_qk(rope, B.grid(fr, hgt, wid), t0, heads, q=xd)
+    got = xd.float().cpu().numpy()
+    ref = oracle.rope3d(exact, oracle.token_positions(fr, hgt, wid, t0), (44, 42, 42), 1e4)
+    if dtype == torch.float32:
+        assert np.abs(got - ref).max() < 2e-5
+    else:  # one bf16 rounding: relative error <= 2^-8 per element
+        assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
+        compare(got, ref, what="rope bf16")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_chunk_pad"])
+def test_kv_append_cache_contents(name):
+    w = get_workload(name)
+    inp = make_inputs(w)
+    r = run_workload(w, inp, with_lse=False)
+    s = r["session"]
+    st = oracle.build_state(w, inp)
+    fs = oracle.frame_stride_for(w.tokens_per_frame)
+    kc = s.cache.k_view().float().cpu().numpy()  # [H][rows][D]
+    vt = s.cache.v_view().float().cpu().numpy()  # [H][D][rows]
+    hw = w.tokens_per_frame
+    for slot in range(w.capacity):
+        if st.ring.slot_frame[slot] < 0:
+            continue
+        rows = slice(slot * fs, slot * fs + hw)
+        k_ref = st.ring.k[slot].transpose(1, 0, 2)  # [H][HW][D]
+        got = kc[:, rows, :]
+        assert (np.abs(got - k_ref) <= np.abs(k_ref) * 2.0 ** -8 + 2e-6).all(), f"slot {slot} keys"
+        v_ref = torch.from_numpy(st.ring.v[slot]).to(torch.bfloat16).float().numpy().transpose(1, 2, 0)
+        np.testing.assert_array_equal(vt[:, :, rows], v_ref)  # values: one RNE rounding, bit-exact
+        if fs > hw:
+            assert (kc[:, slot * fs + hw:(slot + 1) * fs, :] == 0).all()
+            assert (vt[:, :, slot * fs + hw:(slot + 1) * fs] == 0).all()
+
+
+# ------------------------------------------------------------------ attention
+def _oracle_rows(w, inp, heads, rows):
+    st = oracle.build_state(w, inp)
+    out = {}
+    for h in heads:
+        out[h] = oracle.attention_rows(st, h, rows)
+    return out
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_parity_full(name):
+    _print("attention full", name)
+    w = get_workload(name)
+    inp = make_inputs(w)
+    r = run_workload(w, inp)
+    o = r["o"].float().cpu().numpy()
+    lse = r["lse"].cpu().numpy()
+    ref = _oracle_rows(w, inp, range(w.heads), np.arange(w.n_q))
+    for h in range(w.heads):
+        compare(o[:, h], ref[h][0], what=f"{name} head {h}")
+        np.testing.assert_allclose(lse[h], ref[h][1], atol=1e-2, rtol=0)
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_attention_parity_sampled(name):
+    _print("attention sampled", name)
+    w = get_workload(name)
+    inp = make_inputs(w)
+    r = run_workload(w, inp)
+    rows = sample_rows(w)
+    heads = sorted({0, w.heads // 2, w.heads - 1})
+    o = r["o"].float().cpu().numpy()
+    lse = r["lse"].cpu().numpy()
+    assert np.isfinite(o).all()
+    ref = _oracle_rows(w, inp, heads, rows)
+    for h in heads:
+        compare(o[rows, h], ref[h][0], what=f"{name} head {h}")
+        np.testing.assert_allclose(lse[h, rows], ref[h][1], atol=1e-2, rtol=0)
+
+
+@pytest.mark.parametrize("name", ["small_radial", "small_chunk_pad", "stream_wrap_straddle"])
+def test_zero_queries_average_visible_values(name):
+    """Q = 0: every visible key gets the same weight, so O = mean of the visible V rows."""
+    w = get_workload(name)
+    inp = make_inputs(w)
+    r = run_workload(w, inp, q_override=np.zeros_like(inp["q"]))
+    st = oracle.build_state(w, inp)
+    o = r["o"].float().cpu().numpy()
+    q_s = np.arange(w.n_q) % w.tokens_per_frame
+    rows = sample_rows(w, n_random=32)
+    for row in rows:
+        vis = oracle.allowed_mask(w.mask, st.q_pos[row, 0], q_s[row], st.k_t, st.k_s)
+        want = st.v[vis].mean(axis=0)  # [H, D]
+        np.testing.assert_allclose(o[row], want, atol=2e-3, rtol=1e-2, err_msg=f"row {row}")
+
+
+def test_fused_rope_equals_standalone_rope():
+    w = get_workload("small_chunk_pad")
+    inp = make_inputs(w)
+    fused = run_workload(w, inp)
+    qd = to_dev(inp["q"], torch.bfloat16)
+    B.vdit_rope3d_qk(fused["session"].rope, B.grid(w.q_frames, w.frame_h, w.frame_w), w.q_t0, w.heads, q=qd)
+    s = fused["session"]
+    o2 = s.attend(qd, w.q_frames, w.q_t0, fused["plan"], rotate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, fused["o"])
+
+
+def test_chunk_by_chunk_equals_whole_call():
+    """Three 1-frame calls with global start frames give the 3-frame call's output."""
+    w = get_workload("tiny")
+    inp = make_inputs(w)
+    whole = run_workload(w, inp)["o"]
+    s = session_for(w)
+    hw = w.tokens_per_frame
+    parts = []
+    for f in range(3):
+        sl = slice(f * hw, (f + 1) * hw)
+        s.append(to_dev(inp["k"][sl], torch.float32), to_dev(inp["v"][sl], torch.float32), w.q_t0 + f)
+        plan = s.plan(1, w.q_t0 + f)
+        parts.append(s.attend(to_dev(inp["q"][sl], torch.float32), 1, w.q_t0 + f, plan))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts), whole)
+
+
+def test_deterministic():
+    w = get_workload("small_radial")
+    inp = make_inputs(w)
+    a = run_workload(w, inp)
+    b = run_workload(w, inp)
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+    assert (device_plan_words(a["plan"]) == device_plan_words(b["plan"])).all()

@@ -1,0 +1,284 @@
+"""ctypes binding of libvdit (include/vdit.h): same names, argument marshalling only.
+
+Tensors are torch tensors (device memory and streams come from torch); every step of
+the computation runs in the library's HIP kernels.  Loading fails loudly when the
+library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvdit.so")
+
+VDIT_OK, VDIT_ERR_INVALID_ARG, VDIT_ERR_BUFFER_TOO_SMALL, VDIT_ERR_UNSUPPORTED, VDIT_ERR_DEVICE = range(5)
+VDIT_DTYPE_BF16, VDIT_DTYPE_FP32 = 0, 1
+VDIT_MASK_DENSE, VDIT_MASK_CHUNK_CAUSAL, VDIT_MASK_LOG_RADIAL = 0, 1, 2
+VDIT_WHERE_HOST, VDIT_WHERE_DEVICE = 0, 1
+VDIT_PLAN_MAGIC = 0x54494456
+MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, "log_radial": VDIT_MASK_LOG_RADIAL}
+
+# every function declared in include/vdit.h
+EXPORTS = (
+    "vdit_abi_version", "vdit_last_error", "vdit_status_string", "vdit_token_positions",
+    "vdit_rope_table_build", "vdit_rope3d_qk", "vdit_kv_cache_bytes", "vdit_kv_cache_reset",
+    "vdit_kv_append", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_block_attn_fwd",
+)
+
+
+class VditTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64)]
+
+
+class VditGrid(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("height", ctypes.c_int32), ("width", ctypes.c_int32)]
+
+
+class VditRopeCfg(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("dim_t", ctypes.c_int32), ("dim_h", ctypes.c_int32),
+                ("dim_w", ctypes.c_int32), ("theta", ctypes.c_double), ("max_t", ctypes.c_int32),
+                ("max_h", ctypes.c_int32), ("max_w", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("table", ctypes.c_void_p)]
+
+
+class VditKVCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slot_frame_dev", ctypes.c_void_p),
+                ("slot_frame_host", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("tokens_per_frame", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class VditMaskCfg(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("chunk_frames", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("radial_w0", ctypes.c_int32), ("radial_decay_log2", ctypes.c_int32),
+                ("long_range_period", ctypes.c_int32)]
+
+
+class VditError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"vdit status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m video_diffusion_transformer_rope3d_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        pS = ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "vdit_abi_version": (I32, []),
+            "vdit_last_error": (ctypes.c_char_p, []),
+            "vdit_status_string": (ctypes.c_char_p, [I32]),
+            "vdit_token_positions": (I32, [VditGrid, I32, I32, P, P]),
+            "vdit_rope_table_build": (I32, [ctypes.POINTER(VditRopeCfg), P, SZ, pS]),
+            "vdit_rope3d_qk": (I32, [ctypes.POINTER(VditRopeCfg), VditGrid, I32, I32, VditTensor, VditTensor, P]),
+            "vdit_kv_cache_bytes": (I32, [I32, I32, I32, I32, pS, pS]),
+            "vdit_kv_cache_reset": (I32, [ctypes.POINTER(VditKVCache), P]),
+            "vdit_kv_append": (I32, [ctypes.POINTER(VditKVCache), ctypes.POINTER(VditRopeCfg), VditGrid, I32,
+                                     VditTensor, VditTensor, P]),
+            "vdit_plan_qtiles": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(I32)]),
+            "vdit_plan_bound": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(VditKVCache), pS]),
+            "vdit_plan_mask": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(VditKVCache), I32,
+                                     P, SZ, pS, P]),
+            "vdit_block_attn_fwd": (I32, [VditTensor, ctypes.POINTER(VditRopeCfg), VditGrid, I32,
+                                          ctypes.POINTER(VditKVCache), ctypes.POINTER(VditMaskCfg), P,
+                                          ctypes.c_float, VditTensor, P, P]),
+        }
+        for name in EXPORTS:
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = sig[name]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != VDIT_OK:
+        raise VditError(status, lib().vdit_last_error().decode())
+
+
+# ---------------------------------------------------------------- marshalling helpers
+def grid(frames, height, width) -> VditGrid:
+    return VditGrid(frames, height, width)
+
+
+def mask_cfg(kind, chunk_frames=1, tile=128, radial_w0=13, radial_decay_log2=1, long_range_period=8) -> VditMaskCfg:
+    k = MASK_KINDS[kind] if isinstance(kind, str) else int(kind)
+    return VditMaskCfg(k, chunk_frames, tile, radial_w0, radial_decay_log2, long_range_period)
+
+
+def tensor(x) -> VditTensor:
+    """[tokens][heads][channels] torch tensor (bf16 / fp32, channels contiguous)."""
+    import torch
+    if x is None:
+        return VditTensor(None, 0, 0, 0, 0)
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("expected a [tokens][heads][channels] tensor with contiguous channels")
+    dt = {torch.bfloat16: VDIT_DTYPE_BF16, torch.float32: VDIT_DTYPE_FP32}.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    return VditTensor(x.data_ptr(), dt, 0, x.stride(0), x.stride(1))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+# ---------------------------------------------------------------- entry points
+def vdit_abi_version() -> int:
+    return lib().vdit_abi_version()
+
+
+def vdit_status_string(status: int) -> str:
+    return lib().vdit_status_string(status).decode()
+
+
+def vdit_last_error() -> str:
+    return lib().vdit_last_error().decode()
+
+
+def vdit_token_positions(g: VditGrid, t0: int, where: int = VDIT_WHERE_HOST, out=None, stream=None):
+    n = g.frames * g.height * g.width
+    if where == VDIT_WHERE_HOST:
+        out = np.zeros((n, 3), np.int32) if out is None else out
+        _check(lib().vdit_token_positions(g, t0, where, out.ctypes.data, None))
+        return out
+    import torch
+    out = torch.empty((n, 3), dtype=torch.int32, device="cuda") if out is None else out
+    _check(lib().vdit_token_positions(g, t0, where, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def rope_cfg(head_dim, dims, theta, max_t, max_h, max_w, table=None) -> VditRopeCfg:
+    return VditRopeCfg(head_dim, dims[0], dims[1], dims[2], float(theta), max_t, max_h, max_w, 0,
+                       None if table is None else table.data_ptr())
+
+
+def vdit_rope_table_build(cfg: VditRopeCfg) -> np.ndarray:
+    need = ctypes.c_size_t(0)
+    st = lib().vdit_rope_table_build(ctypes.byref(cfg), None, 0, ctypes.byref(need))
+    if st not in (VDIT_OK, VDIT_ERR_BUFFER_TOO_SMALL):
+        _check(st)
+    out = np.zeros(need.value, np.float32)
+    _check(lib().vdit_rope_table_build(ctypes.byref(cfg), out.ctypes.data, out.size, ctypes.byref(need)))
+    return out
+
+
+class Rope:
+    """RoPE configuration plus its device table (built on the host, copied once)."""
+
+    def __init__(self, head_dim, dims, theta, max_t, max_h, max_w, device="cuda"):
+        import torch
+        cfg = rope_cfg(head_dim, dims, theta, max_t, max_h, max_w)
+        self.host_table = vdit_rope_table_build(cfg)
+        self.table = torch.from_numpy(self.host_table).to(device)
+        self.cfg = rope_cfg(head_dim, dims, theta, max_t, max_h, max_w, self.table)
+
+
+def vdit_rope3d_qk(rope: Rope, g: VditGrid, t0: int, heads: int, q=None, k=None, stream=None):
+    _check(lib().vdit_rope3d_qk(ctypes.byref(rope.cfg), g, t0, heads, tensor(q), tensor(k), _stream(stream)))
+
+
+def vdit_kv_cache_bytes(capacity, tokens_per_frame, heads, head_dim):
+    kb, vb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().vdit_kv_cache_bytes(capacity, tokens_per_frame, heads, head_dim, ctypes.byref(kb), ctypes.byref(vb)))
+    return kb.value, vb.value
+
+
+class KVCache:
+    """Caller-side allocation of the ring cache (torch device memory) and its descriptor."""
+
+    def __init__(self, capacity, tokens_per_frame, heads, head_dim, device="cuda", stream=None):
+        import torch
+        kb, vb = vdit_kv_cache_bytes(capacity, tokens_per_frame, heads, head_dim)
+        self.frame_stride = (tokens_per_frame + 7) // 8 * 8
+        self.kv_rows = capacity * self.frame_stride
+        self.k = torch.empty(kb // 2, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty(vb // 2, dtype=torch.bfloat16, device=device)
+        self.slot_dev = torch.empty(capacity, dtype=torch.int32, device=device)
+        self.slot_host = np.full(capacity, -1, np.int32)
+        self.desc = VditKVCache(self.k.data_ptr(), self.v.data_ptr(), self.slot_dev.data_ptr(),
+                                self.slot_host.ctypes.data, capacity, tokens_per_frame, heads, head_dim)
+        vdit_kv_cache_reset(self, stream)
+
+    def k_view(self):
+        """Keys as [heads][kv_rows][head_dim]."""
+        d = self.desc
+        return self.k.view(d.heads, self.kv_rows, d.head_dim)
+
+    def v_view(self):
+        """Values as stored: [heads][head_dim][kv_rows]."""
+        d = self.desc
+        return self.v.view(d.heads, d.head_dim, self.kv_rows)
+
+
+def vdit_kv_cache_reset(cache: KVCache, stream=None):
+    _check(lib().vdit_kv_cache_reset(ctypes.byref(cache.desc), _stream(stream)))
+
+
+def vdit_kv_append(cache: KVCache, rope, g: VditGrid, t0: int, k, v, stream=None):
+    rp = ctypes.byref(rope.cfg) if rope is not None else None
+    _check(lib().vdit_kv_append(ctypes.byref(cache.desc), rp, g, t0, tensor(k), tensor(v), _stream(stream)))
+
+
+def vdit_plan_qtiles(mask: VditMaskCfg, g: VditGrid, q_t0: int) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().vdit_plan_qtiles(ctypes.byref(mask), g, q_t0, ctypes.byref(n)))
+    return n.value
+
+
+def vdit_plan_bound(mask: VditMaskCfg, g: VditGrid, q_t0: int, cache: KVCache) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vdit_plan_bound(ctypes.byref(mask), g, q_t0, ctypes.byref(cache.desc), ctypes.byref(n)))
+    return n.value
+
+
+def vdit_plan_mask(mask: VditMaskCfg, g: VditGrid, q_t0: int, cache: KVCache, where=VDIT_WHERE_HOST,
+                   out=None, stream=None):
+    """Host: returns the exact plan (numpy int32).  Device: writes `out` (or a new int32
+    device tensor of the bound size) and returns it."""
+    bound = vdit_plan_bound(mask, g, q_t0, cache)
+    used = ctypes.c_size_t(0)
+    if where == VDIT_WHERE_HOST:
+        buf = np.zeros(bound, np.int32) if out is None else out
+        _check(lib().vdit_plan_mask(ctypes.byref(mask), g, q_t0, ctypes.byref(cache.desc), where,
+                                    buf.ctypes.data, buf.size, ctypes.byref(used), None))
+        return buf[:used.value]
+    import torch
+    buf = torch.empty(bound, dtype=torch.int32, device="cuda") if out is None else out
+    _check(lib().vdit_plan_mask(ctypes.byref(mask), g, q_t0, ctypes.byref(cache.desc), where,
+                                buf.data_ptr(), buf.numel(), ctypes.byref(used), _stream(stream)))
+    return buf
+
+
+def vdit_block_attn_fwd(q, rope, g: VditGrid, q_t0: int, cache: KVCache, mask: VditMaskCfg, plan_dev,
+                        softmax_scale: float = 0.0, o=None, lse=None, stream=None):
+    import torch
+    o = torch.empty_like(q) if o is None else o
+    rp = ctypes.byref(rope.cfg) if rope is not None else None
+    _check(lib().vdit_block_attn_fwd(tensor(q), rp, g, q_t0, ctypes.byref(cache.desc), ctypes.byref(mask),
+                                     plan_dev.data_ptr(), ctypes.c_float(softmax_scale), tensor(o),
+                                     None if lse is None else lse.data_ptr(), _stream(stream)))
+    return o
+
+
+def plan_fields(plan):
+    """Split plan words (numpy) into (header, qtiles [n,2], row_ptr [n+1], spans [m,2])."""
+    p = np.asarray(plan)
+    nq, ns = int(p[4]), int(p[5])
+    qt = p[8:8 + 2 * nq].reshape(nq, 2)
+    rp = p[8 + 2 * nq:8 + 3 * nq + 1]
+    sp = p[8 + 3 * nq + 1:8 + 3 * nq + 1 + 2 * ns].reshape(ns, 2)
+    return p[:8], qt, rp, sp

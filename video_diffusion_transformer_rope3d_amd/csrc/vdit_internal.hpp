@@ -1,0 +1,195 @@
+// Internal declarations shared by the host API and the HIP kernels of libvdit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vdit.h"
+
+namespace vdit {
+
+// ------------------------------------------------------------------------------------
+// Block-plan geometry.  The same code enumerates query tiles and key spans on the host
+// (vdit_plan_mask with VDIT_WHERE_HOST) and in the device builder kernel, so both emit
+// identical words.
+//
+// Visibility rules: Wave Forcing / WaveRT page (block-causal attention: a block sees
+// itself and the blocks before it, blocks of 3 latent frames starting at multiples of 3)
+// and "DynamicRad: Content-Adaptive Sparse Attention for Long Video Diffusion", section 2
+// (window shrinking exponentially with temporal distance, long-range factor for periodic
+// frames, static-ratio mode).
+// ------------------------------------------------------------------------------------
+struct PlanGeom {
+    int32_t kind, chunk_frames, tile, w0, decay_log2, period;
+    int32_t frames, hw, t0;          // query call: frames of hw tokens from global frame t0
+    int32_t capacity, frame_stride;  // cache
+};
+
+__host__ __device__ inline int32_t frame_stride_of(int32_t tokens_per_frame) {
+    return (tokens_per_frame + 7) / 8 * 8;
+}
+
+// Window of the log-radial rule in tiles: ceil(w0 / 2^(decay_log2 * d)).
+__host__ __device__ inline int32_t radial_window(int32_t d, int32_t w0, int32_t decay_log2) {
+    int64_t sh = (int64_t)d * decay_log2;
+    if (sh >= 40) return w0 > 0 ? 1 : 0;
+    int64_t den = (int64_t)1 << sh;
+    return (int32_t)(((int64_t)w0 + den - 1) >> sh);
+}
+
+// Number of mask units of the call and [first, end) call frames of unit u.
+__host__ __device__ inline int32_t plan_units(const PlanGeom& g) {
+    if (g.frames <= 0) return 0;
+    if (g.kind == VDIT_MASK_DENSE) return 1;
+    if (g.kind == VDIT_MASK_LOG_RADIAL) return g.frames;
+    int32_t c0 = g.t0 / g.chunk_frames, c1 = (g.t0 + g.frames - 1) / g.chunk_frames;
+    return c1 - c0 + 1;
+}
+
+__host__ __device__ inline void plan_unit_frames(const PlanGeom& g, int32_t u, int32_t* f_begin, int32_t* f_end) {
+    if (g.kind == VDIT_MASK_DENSE) {
+        *f_begin = 0;
+        *f_end = g.frames;
+    } else if (g.kind == VDIT_MASK_LOG_RADIAL) {
+        *f_begin = u;
+        *f_end = u + 1;
+    } else {
+        int32_t c = g.t0 / g.chunk_frames + u;
+        int32_t b = c * g.chunk_frames - g.t0, e = (c + 1) * g.chunk_frames - g.t0;
+        *f_begin = b < 0 ? 0 : b;
+        *f_end = e > g.frames ? g.frames : e;
+    }
+}
+
+__host__ __device__ inline int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+__host__ __device__ inline int32_t plan_qtile_count(const PlanGeom& g) {
+    int32_t n = 0, nu = plan_units(g);
+    for (int32_t u = 0; u < nu; ++u) {
+        int32_t fb, fe;
+        plan_unit_frames(g, u, &fb, &fe);
+        n += ceil_div((fe - fb) * g.hw, g.tile);
+    }
+    return n;
+}
+
+// Query tile i: rows [q_start, q_start + q_len), the global frame of its first row and,
+// for the log-radial rule, its spatial tile index inside the frame.
+struct QTile {
+    int32_t q_start, q_len, t_q, unit_first_frame, piece;
+};
+
+__host__ __device__ inline QTile plan_qtile(const PlanGeom& g, int32_t i) {
+    QTile qt{0, 0, 0, 0, 0};
+    int32_t nu = plan_units(g);
+    for (int32_t u = 0; u < nu; ++u) {
+        int32_t fb, fe;
+        plan_unit_frames(g, u, &fb, &fe);
+        int32_t len = (fe - fb) * g.hw;
+        int32_t nt = ceil_div(len, g.tile);
+        if (i < nt) {
+            int32_t off = i * g.tile;
+            qt.q_start = fb * g.hw + off;
+            qt.q_len = (len - off) < g.tile ? (len - off) : g.tile;
+            qt.unit_first_frame = fb;
+            qt.t_q = g.t0 + fb + off / g.hw;
+            qt.piece = i;
+            return qt;
+        }
+        i -= nt;
+    }
+    return qt;
+}
+
+// Within-frame key range [a, b) visible from query tile qt in a slot holding frame t;
+// returns false when the slot contributes nothing.
+__host__ __device__ inline bool plan_slot_range(const PlanGeom& g, const QTile& qt, int32_t t, int32_t* a,
+                                                int32_t* b) {
+    if (t < 0) return false;
+    if (g.kind == VDIT_MASK_DENSE) {
+        *a = 0;
+        *b = g.hw;
+        return true;
+    }
+    if (g.kind == VDIT_MASK_CHUNK_CAUSAL) {
+        if (t / g.chunk_frames > qt.t_q / g.chunk_frames) return false;
+        *a = 0;
+        *b = g.hw;
+        return true;
+    }
+    int32_t d = t > qt.t_q ? t - qt.t_q : qt.t_q - t;
+    if (d == 0 || (g.period > 0 && d % g.period == 0)) {
+        *a = 0;
+        *b = g.hw;
+        return true;
+    }
+    int32_t wd = radial_window(d, g.w0, g.decay_log2);
+    int32_t ntiles = ceil_div(g.hw, g.tile);
+    int32_t lo = qt.piece - wd, hi = qt.piece + wd;
+    if (lo < 0) lo = 0;
+    if (hi > ntiles - 1) hi = ntiles - 1;
+    *a = lo * g.tile;
+    int32_t e = (hi + 1) * g.tile;
+    *b = e < g.hw ? e : g.hw;
+    return *b > *a;
+}
+
+// Emits the maximal ascending runs of visible physical key indices of query tile qt.
+template <class Emit>
+__host__ __device__ inline void plan_tile_spans(const PlanGeom& g, const int32_t* slot_frame, const QTile& qt,
+                                                Emit&& emit) {
+    int32_t run_start = 0, run_end = -1;
+    for (int32_t slot = 0; slot < g.capacity; ++slot) {
+        int32_t a, b;
+        if (!plan_slot_range(g, qt, slot_frame[slot], &a, &b)) continue;
+        int32_t s0 = slot * g.frame_stride + a, s1 = slot * g.frame_stride + b;
+        if (s0 == run_end) {
+            run_end = s1;
+        } else {
+            if (run_end >= 0) emit(run_start, run_end - run_start);
+            run_start = s0;
+            run_end = s1;
+        }
+    }
+    if (run_end >= 0) emit(run_start, run_end - run_start);
+}
+
+__host__ __device__ inline size_t plan_bound_words(int32_t n_qtiles, int32_t capacity) {
+    return (size_t)VDIT_PLAN_HEADER_WORDS + 2 * (size_t)n_qtiles + (size_t)n_qtiles + 1 +
+           2 * (size_t)n_qtiles * (size_t)capacity;
+}
+
+// ------------------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files).  Arguments are validated by the caller.
+// ------------------------------------------------------------------------------------
+struct RopeDev {
+    const float2* tab_t;
+    const float2* tab_h;
+    const float2* tab_w;
+    int32_t pairs_t, pairs_h, pairs_w;
+};
+
+hipError_t launch_positions(vdit_grid grid, int32_t t0, int32_t* out, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+hipError_t launch_rope_inplace(const RopeDev& r, vdit_grid grid, int32_t t0, int32_t heads, int32_t head_dim,
+                               vdit_tensor x, hipStream_t s);
+hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
+                            vdit_tensor v, hipStream_t s);
+hipError_t launch_plan_build(const PlanGeom& g, const int32_t* slot_frame_dev, int32_t n_qtiles, int32_t* plan,
+                             hipStream_t s);
+
+struct AttnLaunch {
+    vdit_tensor q, o;
+    float* lse;
+    const void* kc;
+    const void* vt;
+    int64_t kv_rows;
+    const int32_t* plan;
+    RopeDev rope;
+    bool has_rope;
+    int32_t hw, wf, t0, n_tokens, heads, head_dim, n_qtiles;
+    float scale_log2;
+};
+hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace vdit

@@ -1,0 +1,288 @@
+// Bandwidth-bound kernels of libvdit: token positions, RoPE3D in place, the ring KV-cache
+// append (keys rotated at their global positions, values transposed) and the device
+// block-plan builder.
+#include "vdit_bf16.hpp"
+#include "vdit_internal.hpp"
+
+namespace vdit {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- positions: global time index = start frame + local frame ("Accelerating Video
+// Generation Inference ... Using a Global Time Index", section 2.B).
+__global__ void positions_kernel(int32_t n, int32_t hw, int32_t width, int32_t t0, int32_t* out) {
+    int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    int32_t s = i % hw;
+    out[3 * i + 0] = t0 + i / hw;
+    out[3 * i + 1] = s / width;
+    out[3 * i + 2] = s % width;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = value;
+}
+
+// Loads 8 channels starting at `ch` of one token/head into fp32.
+template <bool F32>
+__device__ inline void load8(const void* base, int64_t off, float x[8]) {
+    if constexpr (F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+        float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
+        unpack_bf16x8(u, x);
+    }
+}
+
+template <bool F32>
+__device__ inline void store8(void* base, int64_t off, const float x[8]) {
+    if constexpr (F32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
+        p[0] = make_float4(x[0], x[1], x[2], x[3]);
+        p[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + off) = pack_bf16x8(x);
+    }
+}
+
+// ---- RoPE3D in place: one thread per (token, head, 8-channel chunk).
+template <bool F32>
+__global__ void rope_inplace_kernel(RopeDev r, int32_t n, int32_t hw, int32_t width, int32_t t0, int32_t heads,
+                                    int32_t head_dim, void* x, int64_t st, int64_t sh) {
+    int32_t chunks = head_dim / 8;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)n * heads * chunks) return;
+    int32_t c = (int32_t)(i % chunks);
+    int64_t th = i / chunks;
+    int32_t h = (int32_t)(th % heads);
+    int32_t tok = (int32_t)(th / heads);
+    int32_t s = tok % hw;
+    int32_t pos_t = t0 + tok / hw, pos_h = s / width, pos_w = s % width;
+    int64_t off = (int64_t)tok * st + (int64_t)h * sh + c * 8;
+    float v[8];
+    load8<F32>(x, off, v);
+    rope_rotate8(r, c * 4, pos_t, pos_h, pos_w, v);
+    store8<F32>(x, off, v);
+}
+
+// ---- KV append.  Block = 64 tokens x one head.  Keys: rotated (optional) and written
+// to k[h][phys][:].  Values: staged in LDS and written transposed to v[h][d][phys] so that
+// consecutive lanes write consecutive keys of one channel row.
+constexpr int kAppendTok = 64;
+
+template <int D, bool F32>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has_rope, int32_t n, int32_t hw,
+                                                             int32_t width, int32_t t0, int32_t capacity,
+                                                             int32_t frame_stride, int64_t kv_rows,
+                                                             const void* k, int64_t k_st, int64_t k_sh,
+                                                             const void* v, int64_t v_st, int64_t v_sh,
+                                                             uint16_t* kc, uint16_t* vt, int32_t* slot_frame,
+                                                             int32_t frames) {
+    constexpr int CH = D / 8;
+    constexpr int PITCH = D + 2;  // bf16 elements per LDS row, odd dword count per row
+    __shared__ uint16_t sv[kAppendTok * PITCH];
+    const int32_t h = blockIdx.y;
+    const int32_t n0 = blockIdx.x * kAppendTok;
+    const int tid = threadIdx.x;
+
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid < frames) slot_frame[(t0 + tid) % capacity] = t0 + tid;
+
+    for (int c = tid; c < kAppendTok * CH; c += kThreads) {
+        int32_t lt = c / CH, ch = c % CH;
+        int32_t tok = n0 + lt;
+        if (tok >= n) continue;
+        int32_t f = tok / hw, s = tok % hw;
+        int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
+        float x[8];
+        load8<F32>(k, (int64_t)tok * k_st + (int64_t)h * k_sh + ch * 8, x);
+        if (has_rope) rope_rotate8(r, ch * 4, t0 + f, s / width, s % width, x);
+        *reinterpret_cast<u32x4*>(kc + ((int64_t)h * kv_rows + phys) * D + ch * 8) = pack_bf16x8(x);
+        load8<F32>(v, (int64_t)tok * v_st + (int64_t)h * v_sh + ch * 8, x);
+        u32x4 pv = pack_bf16x8(x);
+        uint16_t* row = sv + lt * PITCH + ch * 8;
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(&pv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) row[e] = src[e];
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int32_t tok = n0 + lane;
+    if (tok < n) {
+        int32_t f = tok / hw, s = tok % hw;
+        int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
+        for (int d = wave; d < D; d += kThreads / 64) vt[((int64_t)h * D + d) * kv_rows + phys] = sv[lane * PITCH + d];
+    }
+}
+
+// Zeroes the padding tokens [hw, frame_stride) of the written slots in k and v.
+template <int D>
+__global__ void kv_zero_pad_kernel(int32_t hw, int32_t frame_stride, int32_t t0, int32_t capacity, int64_t kv_rows,
+                                   uint16_t* kc, uint16_t* vt) {
+    const int32_t f = blockIdx.x, h = blockIdx.y;
+    const int32_t pad = frame_stride - hw;
+    const int64_t base = (int64_t)((t0 + f) % capacity) * frame_stride + hw;
+    for (int i = threadIdx.x; i < pad * D; i += blockDim.x) {
+        int32_t p = i / D, d = i % D;
+        kc[((int64_t)h * kv_rows + base + p) * D + d] = 0;
+        vt[((int64_t)h * D + d) * kv_rows + base + p] = 0;
+    }
+}
+
+// ---- device plan builder: one workgroup.  Pass 1 counts spans per query tile, an
+// exclusive scan turns counts into row pointers, pass 2 writes the spans.  All integer,
+// so the words equal the host builder's.
+constexpr int kPlanThreads = 256;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_build_kernel(PlanGeom g, const int32_t* slot_frame, int32_t nq,
+                                                                  int32_t* plan) {
+    __shared__ int32_t s_slot[1024];
+    __shared__ int32_t s_scan[kPlanThreads];
+    __shared__ long long s_pairs[kPlanThreads];
+    __shared__ int32_t s_carry;
+    const int tid = threadIdx.x;
+    const int32_t* sf = slot_frame;
+    if (g.capacity <= 1024) {
+        for (int i = tid; i < g.capacity; i += kPlanThreads) s_slot[i] = slot_frame[i];
+        sf = s_slot;
+    }
+    int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
+    int32_t* row_ptr = qtiles + 2 * nq;
+    int32_t* spans = row_ptr + nq + 1;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+
+    long long pairs = 0;
+    // pass 1 + scan, in chunks of kPlanThreads tiles
+    for (int32_t base = 0; base < nq; base += kPlanThreads) {
+        int32_t i = base + tid;
+        int32_t cnt = 0;
+        if (i < nq) {
+            QTile qt = plan_qtile(g, i);
+            qtiles[2 * i] = qt.q_start;
+            qtiles[2 * i + 1] = qt.q_len;
+            long long keys = 0;
+            plan_tile_spans(g, sf, qt, [&](int32_t, int32_t len) {
+                ++cnt;
+                keys += len;
+            });
+            pairs += keys * qt.q_len;
+        }
+        s_scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < kPlanThreads; off <<= 1) {
+            int32_t add = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += add;
+            __syncthreads();
+        }
+        if (i < nq) row_ptr[i + 1] = s_carry + s_scan[tid];
+        __syncthreads();
+        if (tid == kPlanThreads - 1) s_carry += s_scan[tid];
+        __syncthreads();
+    }
+    if (tid == 0) row_ptr[0] = 0;
+    __threadfence_block();
+    __syncthreads();
+    // pass 2
+    for (int32_t i = tid; i < nq; i += kPlanThreads) {
+        QTile qt = plan_qtile(g, i);
+        int32_t k = i == 0 ? 0 : row_ptr[i];
+        plan_tile_spans(g, sf, qt, [&](int32_t s0, int32_t len) {
+            spans[2 * k] = s0;
+            spans[2 * k + 1] = len;
+            ++k;
+        });
+    }
+    s_pairs[tid] = pairs;
+    __syncthreads();
+    for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) s_pairs[tid] += s_pairs[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        unsigned long long tot = (unsigned long long)s_pairs[0];
+        plan[0] = (int32_t)VDIT_PLAN_MAGIC;
+        plan[1] = VDIT_PLAN_VERSION;
+        plan[2] = g.kind;
+        plan[3] = g.tile;
+        plan[4] = nq;
+        plan[5] = s_carry;
+        plan[6] = (int32_t)(uint32_t)(tot & 0xFFFFFFFFull);
+        plan[7] = (int32_t)(uint32_t)(tot >> 32);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_positions(vdit_grid grid, int32_t t0, int32_t* out, hipStream_t s) {
+    int32_t hw = grid.height * grid.width, n = grid.frames * hw;
+    if (n == 0) return hipSuccess;
+    positions_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(n, hw, grid.width, t0, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    fill_i32_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(p, value, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_inplace(const RopeDev& r, vdit_grid grid, int32_t t0, int32_t heads, int32_t head_dim,
+                               vdit_tensor x, hipStream_t s) {
+    int32_t hw = grid.height * grid.width, n = grid.frames * hw;
+    int64_t total = (int64_t)n * heads * (head_dim / 8);
+    unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
+    if (x.dtype == VDIT_DTYPE_FP32)
+        rope_inplace_kernel<true><<<blocks, kThreads, 0, s>>>(r, n, hw, grid.width, t0, heads, head_dim, x.data,
+                                                              x.stride_token, x.stride_head);
+    else
+        rope_inplace_kernel<false><<<blocks, kThreads, 0, s>>>(r, n, hw, grid.width, t0, heads, head_dim, x.data,
+                                                               x.stride_token, x.stride_head);
+    return hipGetLastError();
+}
+
+template <int D, bool F32>
+static void append_d(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
+                     vdit_tensor v, hipStream_t s) {
+    int32_t hw = c.tokens_per_frame, n = grid.frames * hw;
+    int32_t fs = frame_stride_of(hw);
+    int64_t kv_rows = (int64_t)c.capacity * fs;
+    dim3 blocks((n + kAppendTok - 1) / kAppendTok, c.heads);
+    RopeDev rr = r ? *r : RopeDev{};
+    kv_append_kernel<D, F32><<<blocks, kThreads, 0, s>>>(
+        rr, r != nullptr, n, hw, grid.width, t0, c.capacity, fs, kv_rows, k.data, k.stride_token, k.stride_head,
+        v.data, v.stride_token, v.stride_head, static_cast<uint16_t*>(c.k), static_cast<uint16_t*>(c.v),
+        c.slot_frame_dev, grid.frames);
+    if (fs > hw)
+        kv_zero_pad_kernel<D><<<dim3(grid.frames, c.heads), kThreads, 0, s>>>(
+            hw, fs, t0, c.capacity, kv_rows, static_cast<uint16_t*>(c.k), static_cast<uint16_t*>(c.v));
+}
+
+hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
+                            vdit_tensor v, hipStream_t s) {
+    // K and V share one kernel: both must have the same dtype
+    if (k.dtype != v.dtype) return hipErrorInvalidValue;
+    bool f32 = k.dtype == VDIT_DTYPE_FP32;
+    if (c.head_dim == 128) {
+        if (f32) append_d<128, true>(c, r, grid, t0, k, v, s);
+        else append_d<128, false>(c, r, grid, t0, k, v, s);
+    } else {
+        if (f32) append_d<64, true>(c, r, grid, t0, k, v, s);
+        else append_d<64, false>(c, r, grid, t0, k, v, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_build(const PlanGeom& g, const int32_t* slot_frame_dev, int32_t n_qtiles, int32_t* plan,
+                             hipStream_t s) {
+    plan_build_kernel<<<1, kPlanThreads, 0, s>>>(g, slot_frame_dev, n_qtiles, plan);
+    return hipGetLastError();
+}
+
+}  // namespace vdit
