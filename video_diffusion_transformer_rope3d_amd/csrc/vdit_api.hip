@@ -113,8 +113,9 @@ int check_cache(const vdit_kv_cache* c) {
                     c->capacity, c->tokens_per_frame, c->heads);
     if (c->head_dim != 64 && c->head_dim != 128)
         return fail(VDIT_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
-    if ((int64_t)c->capacity * frame_stride_of(c->tokens_per_frame) > INT32_MAX)
-        return fail(VDIT_ERR_INVALID_ARG, "cache has more than 2^31-1 key rows");
+    // one head's K (or V^T) slice is addressed with 32-bit buffer offsets
+    if ((int64_t)c->capacity * frame_stride_of(c->tokens_per_frame) * c->head_dim * 2 > INT32_MAX)
+        return fail(VDIT_ERR_UNSUPPORTED, "one head of the cache exceeds 2 GiB");
     return VDIT_OK;
 }
 

@@ -12,6 +12,8 @@
 // MFMA is chosen (bits 2 and 3 of the S row index swapped) so that the bf16 P operand is
 // taken from the S accumulator registers as they are and V^T is read from LDS with one
 // 16-byte read per lane.
+#include <type_traits>
+
 #include "vdit_bf16.hpp"
 #include "vdit_internal.hpp"
 
@@ -46,62 +48,100 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Keeps the instruction scheduler from moving anything across this point, so that the
+// fragment reads of one phase are not hoisted into the previous one (register pressure).
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // swap bits 2 and 3
 __device__ inline int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
+// LDS stage = K tile [kBN keys][D] + V^T tile [D][kBN keys], both dense, in 16-byte chunks.
+// Chunk c of row r is stored at chunk position c ^ swz(r), so that the 16-byte fragment
+// reads of 16 consecutive lanes (16 different rows, same c) hit 16 different bank groups.
+// Tiles are filled by global_load_lds_dwordx4: lane l of a wave writes the 16 bytes at
+// LDS base + 16 l, so each lane loads the global chunk that belongs at its LDS position.
 template <int D>
 struct Tile {
-    static constexpr int KP = D + 8;    // LDS pitch of a K row (elements)
-    static constexpr int VP = kBN + 8;  // LDS pitch of a V^T row
-    static constexpr int K_ELEMS = kBN * KP;
-    static constexpr int V_ELEMS = D * VP;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int K_LOADS = kBN * D / 8 / kThreads;  // 16-byte loads per thread
-    static constexpr int V_LOADS = D * kBN / 8 / kThreads;
+    static constexpr int KCH = D / 8;    // 16-byte chunks per K row
+    static constexpr int VCH = kBN / 8;  // 16-byte chunks per V^T row
+    static constexpr int K_BYTES = kBN * D * 2;
+    static constexpr int V_BYTES = D * kBN * 2;
+    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int K_LOADS = kBN * KCH / kThreads;  // direct loads per thread
+    static constexpr int V_LOADS = D * VCH / kThreads;
 };
 
+template <int CH>
+__device__ inline int swz(int r) {
+    return CH == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Per-lane constants of the tile DMA.  Load i of wave w fills 1 KB block b = 4 i + w of a
+// tile whose rows hold CH chunks: the lane writes row b * (64 / CH) + lane / CH, chunk
+// position lane % CH, i.e. data chunk (lane % CH) ^ swz(row); swz(row) depends on the lane
+// and on w only, so each lane has one byte offset per tile: rib * row_pitch + chunk * 16.
+template <int CH>
+struct DmaLane {
+    int rib;    // row inside the 1 KB block
+    int chunk;  // data chunk this lane copies
+};
+
+template <int CH>
+__device__ inline DmaLane<CH> dma_lane(int wave, int lane) {
+    constexpr int RPB = 64 / CH;
+    DmaLane<CH> d;
+    d.rib = lane / CH;
+    // swz(b * RPB + rib) with b = 4 i + wave
+    const int s = CH == 16 ? ((wave & 3) << 2) | d.rib : ((wave & 1) << 2) | (d.rib >> 1);
+    d.chunk = (lane % CH) ^ s;
+    (void)RPB;
+    return d;
+}
+
+// Buffer descriptor over one head's K rows or V^T rows (raw, byte-addressed).  Loads through
+// it are range-checked by the hardware against `bytes`.
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Enqueues the DMA of K rows [k0, k0 + kBN) and the V^T columns of the same keys into
+// `stage`.  In a tail tile, keys at or beyond kend are replaced by in-bounds keys of the
+// span (their scores are masked) and V^T chunks by the last chunk holding a valid key.
+// Uniform parts of the addresses go to the scalar offset, the lane's part to voffset.
 template <int D>
-__device__ inline void load_tile(const AttnArgs& a, int h, int k0, int kend, int tid, u32x4* kr, u32x4* vr) {
+__device__ inline void load_tile_lds(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t vpitch, int k0,
+                                     int kend, int wave, const DmaLane<D / 8>& kl, const DmaLane<kBN / 8>& vl,
+                                     char* stage) {
     using T = Tile<D>;
-    const uint16_t* kbase = a.kc + (int64_t)h * a.kv_rows * D;
+    constexpr int KRPB = 64 / T::KCH, VRPB = 64 / T::VCH;
+    // every address stays inside the span: scalar offset = tile start k0 (< kend), the lane's
+    // row delta is clamped to kend - 1 - k0 >= 0
+    const int last = kend - 1 - k0;
 #pragma unroll
-    for (int r = 0; r < T::K_LOADS; ++r) {
-        int c = tid + kThreads * r;
-        int row = c / (D / 8), col = c % (D / 8);
-        int key = k0 + row;
-        key = key < kend ? key : kend - 1;
-        kr[r] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * D + col * 8);
+    for (int i = 0; i < T::K_LOADS; ++i) {
+        const int blk = i * kWaves + wave;
+        const int rowd = min(blk * KRPB + kl.rib, last);
+        const uint32_t voff = (uint32_t)rowd * (D * 2) + kl.chunk * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + blk * 1024), 16, voff,
+                                                 (uint32_t)k0 * (D * 2), 0, 0);
     }
-    const uint16_t* vbase = a.vt + (int64_t)h * D * a.kv_rows;
+    const int vkey = min(k0 + vl.chunk * 8, (kend - 1) & ~7);  // >= k0: k0 is a multiple of 8
+    const uint32_t vcol = (uint32_t)(vkey - k0) * 2;
 #pragma unroll
-    for (int r = 0; r < T::V_LOADS; ++r) {
-        int c = tid + kThreads * r;
-        int drow = c / (kBN / 8), col = c % (kBN / 8);
-        int key = k0 + col * 8;
-        key = key < kend ? key : ((kend - 1) & ~7);
-        vr[r] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)drow * a.kv_rows + key);
+    for (int i = 0; i < T::V_LOADS; ++i) {
+        const int blk = i * kWaves + wave;
+        const uint32_t voff = (uint32_t)vl.rib * vpitch + vcol;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + T::K_BYTES + blk * 1024), 16, voff,
+                                                 (uint32_t)(blk * VRPB) * vpitch + (uint32_t)k0 * 2, 0, 0);
     }
 }
 
-template <int D>
-__device__ inline void store_tile(uint16_t* stage, int tid, const u32x4* kr, const u32x4* vr) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int r = 0; r < T::K_LOADS; ++r) {
-        int c = tid + kThreads * r;
-        int row = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<u32x4*>(stage + row * T::KP + col * 8) = kr[r];
-    }
-    uint16_t* vs = stage + T::K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < T::V_LOADS; ++r) {
-        int c = tid + kThreads * r;
-        int drow = c / (kBN / 8), col = c % (kBN / 8);
-        *reinterpret_cast<u32x4*>(vs + drow * T::VP + col * 8) = vr[r];
-    }
-}
+__device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Logical work item of this workgroup.  Workgroups are dispatched round-robin over the
 // 8 XCDs; renumber so that each XCD gets a contiguous range of (head, query tile) items,
@@ -118,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     using T = Tile<D>;
     constexpr int KS = D / 16;  // k-steps of the QK^T contraction
     constexpr int DB = D / 32;  // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -173,19 +213,124 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     f32x16 oacc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-    float m_run = -1e30f, l_run = 0.f;
+    // Running max of the raw scores used as the exponent base.  It is only raised when a
+    // tile's max exceeds it by more than kLazy (in log2 units), so most tiles skip the
+    // rescale of O; p = exp2((s - m) * c) then stays below 2^kLazy.
+    constexpr float kLazy = 8.0f;
+    const float c = a.scale_log2;
+    const float lazy_raw = kLazy / c;
+    float m_run = -INFINITY, l_run = 0.f;
 
     if (sp_begin < sp_end) {
         int span = sp_begin;
         int k0 = spans[2 * span], kend = k0 + spans[2 * span + 1];
-        u32x4 kr[T::K_LOADS], vr[T::V_LOADS];
-        load_tile<D>(a, h, k0, kend, tid, kr, vr);
-        store_tile<D>(smem, tid, kr, vr);
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        const DmaLane<D / 8> kl = dma_lane<D / 8>(wave_u, lane);
+        const DmaLane<kBN / 8> vl = dma_lane<kBN / 8>(wave_u, lane);
+        const uint32_t head_bytes = (uint32_t)(a.kv_rows * D * 2);
+        const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.kc + (int64_t)h * a.kv_rows * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.vt + (int64_t)h * D * a.kv_rows, head_bytes);
+        const uint32_t vpitch = (uint32_t)(a.kv_rows * 2);
+        load_tile_lds<D>(rk, rv, vpitch, k0, kend, wave_u, kl, vl, smem);
+        wait_tile_loads();
         __syncthreads();
         int buf = 0;
-        const int krow_lane = swap23(qi);
+        // per-lane fragment addresses (bytes inside a stage)
+        const int krow = swap23(qi);  // S row qi holds key krow of each 32-key block
+        const int kswz = swz<T::KCH>(krow);
+        const int vswz = swz<T::VCH>(qi);
+
+        auto body = [&]() {
+            const char* kst = smem + buf * T::STAGE;
+            const char* vst = kst + T::K_BYTES;
+            auto read_k = [&](int ks, int kb) {
+                return *reinterpret_cast<const bf16x8*>(kst + (kb * 32 + krow) * (T::KCH * 16) +
+                                                        (((2 * ks + g) ^ kswz) * 16));
+            };
+            auto read_v = [&](int j, int db) {
+                return *reinterpret_cast<const bf16x8*>(vst + (db * 32 + qi) * (T::VCH * 16) +
+                                                        (((2 * j + g) ^ vswz) * 16));
+            };
+            // S^T = K Q^T over 2 blocks of 32 keys, fragments read half a tile ahead
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            constexpr int KH = KS / 2;
+            bf16x8 kf[KH][2];
+#pragma unroll
+            for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) kf[ks][kb] = read_k(ks, kb);
+            sched_fence();
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        sacc[kb] = mfma32(kf[ks][kb], qreg[half * KH + ks], sacc[kb]);
+                        if (half == 0) kf[ks][kb] = read_k(KH + ks, kb);
+                    }
+                sched_fence();
+            }
+            // first half of the V^T fragments, read while the softmax runs
+            bf16x8 vf[2][DB];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) vf[j][db] = read_v(j, db);
+            sched_fence();
+            // online softmax
+            if (k0 + kBN > kend) {  // ragged last tile of a span: hide keys >= kend
+                asm volatile("");     // keeps this a branch instead of selects on every tile
+                const int lim = kend - k0 - g * 8;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) sacc[kb][r] = -INFINITY;
+            }
+            float mt = sacc[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            if (__any(mt > m_run + lazy_raw)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = fast_exp2((m_run - m_new) * c);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            }
+            const float mc = -m_run * c;
+            bf16x8 pk[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = fast_exp2(__builtin_fmaf(sacc[j >> 1][(j & 1) * 8 + e], c, mc));
+                    l_run += p[e];
+                }
+                pk[j] = __builtin_bit_cast(bf16x8, pack_bf16x8(p));
+            }
+            sched_fence();
+            // O^T += V^T P^T
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    oacc[db] = mfma32(vf[j][db], pk[j], oacc[db]);
+                    vf[j][db] = read_v(j + 2, db);
+                }
+            sched_fence();
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] = mfma32(vf[j][db], pk[j + 2], oacc[db]);
+        };
+
         while (true) {
-            // next tile
             int nk0 = k0 + kBN, nkend = kend, nspan = span;
             if (nk0 >= kend) {
                 ++nspan;
@@ -195,75 +340,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
                 }
             }
             const bool has_next = nspan < sp_end;
-            if (has_next) load_tile<D>(a, h, nk0, nkend, tid, kr, vr);
-
-            const uint16_t* ks_lds = smem + buf * T::STAGE;
-            const uint16_t* vs_lds = ks_lds + T::K_ELEMS;
-            // S^T = K Q^T for 2 blocks of 32 keys
-            f32x16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sacc[kb] = f32x16{};
-                const uint16_t* kp = ks_lds + (kb * 32 + krow_lane) * T::KP + g * 8;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    bf16x8 kv = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
-                    sacc[kb] = mfma32(kv, qreg[ks], sacc[kb]);
-                }
-            }
-            // online softmax (log2 domain)
-            float mt = -INFINITY;
-            const bool tail = k0 + kBN > kend;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = sacc[kb][r] * a.scale_log2;
-                    if (tail) {
-                        int key = k0 + kb * 32 + (r >> 3) * 16 + g * 8 + (r & 7);
-                        x = key < kend ? x : -INFINITY;
-                    }
-                    sacc[kb][r] = x;
-                    mt = fmaxf(mt, x);
-                }
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            float rs = 0.f;
-            bf16x8 pk[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    float p[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        p[e] = fast_exp2(sacc[kb][hh * 8 + e] - m_new);
-                        rs += p[e];
-                    }
-                    pk[kb][hh] = __builtin_bit_cast(bf16x8, pack_bf16x8(p));
-                }
-            }
-            l_run = l_run * alpha + rs;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-            // O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const uint16_t* vp = vs_lds + (db * 32 + qi) * T::VP + g * 8;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        bf16x8 vv = *reinterpret_cast<const bf16x8*>(vp + kb * 32 + hh * 16);
-                        oacc[db] = mfma32(vv, pk[kb][hh], oacc[db]);
-                    }
-                }
-            }
+            if (has_next) load_tile_lds<D>(rk, rv, vpitch, nk0, nkend, wave_u, kl, vl, smem + (buf ^ 1) * T::STAGE);
+            body();
             if (!has_next) break;
-            store_tile<D>(smem + (buf ^ 1) * T::STAGE, tid, kr, vr);
+            wait_tile_loads();
             __syncthreads();
             buf ^= 1;
             k0 = nk0;
@@ -293,7 +373,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
             }
         }
         if (a.lse && g == 0)
-            a.lse[(int64_t)h * a.n_tokens + row] = l > 0.f ? (m_run + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+            a.lse[(int64_t)h * a.n_tokens + row] =
+                l > 0.f ? (m_run * c + __log2f(l)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
