@@ -35,7 +35,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan13b_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=0, help="query rows of the oracle sample (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (whole heads are added until reached)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run one device-to-device copy of MIB MiB before timing (HBM counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="offline: turn two rocprofv3 counter_collection CSVs into profiles/attn_fwd_traffic.json")
+    ap.add_argument("--traffic-copy-mib", type=int, default=256)
+    ap.add_argument("--traffic-command", default="")
     return ap.parse_args()
 
 
@@ -57,8 +64,9 @@ def traffic_per_launch():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inputs, rows_wanted):
-    """The fp64 oracle on a bounded sample of the same workload, on this host's cores."""
+def cpu_baseline(w, inputs, seconds):
+    """The fp64 oracle on a bounded sample of the same workload, on this host's cores:
+    whole heads (all query rows against all cached keys) until `seconds` have elapsed."""
     import numpy as np
     import oracle
     try:
@@ -67,24 +75,65 @@ def cpu_baseline(w, inputs, rows_wanted):
     except Exception:  # pragma: no cover
         cores = 1
     st = oracle.build_state(w, inputs)
-    n_keys = len(st.k_phys)
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(w.n_q, size=min(rows_wanted, w.n_q), replace=False))
-    t = time.perf_counter()
-    oracle.attention_rows(st, 0, rows)
-    dt = time.perf_counter() - t
-    # visible pairs of the sampled rows (every row of this workload sees all cached keys
-    # when the rule is chunk-causal over the whole ring; count exactly from the mask)
     q_s = np.arange(w.n_q) % w.tokens_per_frame
-    vis = oracle.allowed_mask(w.mask, st.q_pos[rows, 0][:, None], q_s[rows][:, None], st.k_t[None], st.k_s[None])
-    flop = 4.0 * w.head_dim * float(vis.sum())
-    return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"head 0, {len(rows)} of {w.n_q} query rows against {n_keys} cached keys: RoPE of the "
-                       f"rows, element mask, fp64 masked softmax attention ({dt:.1f} s); ring build excluded")
+    vis = oracle.allowed_mask(w.mask, st.q_pos[:, 0][:, None], q_s[:, None], st.k_t[None], st.k_s[None])
+    flop_per_head = 4.0 * w.head_dim * float(vis.sum())
+    spent, heads = 0.0, 0
+    while spent < seconds and heads < 4 * w.heads:  # whole heads, cycling, until the budget is used
+        t = time.perf_counter()
+        oracle.attention_rows(st, heads % w.heads)
+        spent += time.perf_counter() - t
+        heads += 1
+    return dict(value=flop_per_head * heads / spent / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"{heads} head passes ({w.heads} heads per chunk), each all {w.n_q} query rows against "
+                       f"{len(st.k_phys)} cached keys: RoPE of Q, element mask, fp64 masked softmax attention "
+                       f"({spent:.1f} s); the ring build (K rotation of all heads) is excluded")
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib, command):
+    """Per-launch HBM bytes of the attention kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the device-to-device copy of copy_mib MiB made by --calibrate-copy."""
+    import csv
+
+    def per_kernel(path, counter, needle):
+        vals = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter and needle in r.get("Kernel_Name", ""):
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} sample of a kernel matching {needle!r} in {path}")
+        return vals
+
+    attn_fetch = per_kernel(fetch_csv, "FETCH_SIZE", "attn_fwd_kernel")
+    attn_write = per_kernel(write_csv, "WRITE_SIZE", "attn_fwd_kernel")
+    # the calibration copy is the largest copy dispatch of the run
+    copy_fetch = max(per_kernel(fetch_csv, "FETCH_SIZE", "copyBuffer"))
+    copy_write = max(per_kernel(write_csv, "WRITE_SIZE", "copyBuffer"))
+    copy_bytes = copy_mib * 2 ** 20
+    f_fetch = copy_bytes / (copy_fetch * 1024)
+    f_write = copy_bytes / (copy_write * 1024)
+    fetch_kib = sum(attn_fetch) / len(attn_fetch)
+    write_kib = sum(attn_write) / len(attn_write)
+    hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
+    out = {"kernel": "attn_fwd_kernel", "kernel_source_sha256": source_sha(ATTN_SRC),
+           "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+           "dispatches": [len(attn_fetch), len(attn_write)],
+           "copy_calibration": {"bytes": copy_bytes, "fetch_kib": copy_fetch, "write_kib": copy_write,
+                                "fetch_factor": f_fetch, "write_factor": f_write},
+           "hbm_bytes_per_launch": hbm, "command": command}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.traffic_copy_mib, args.traffic_command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -124,6 +173,14 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -172,8 +229,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or 1024
-        result["cpu_baseline"] = cpu_baseline(w, inputs, rows)
+        result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
