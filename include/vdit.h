@@ -214,8 +214,17 @@ int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, co
  *   natural-log log-sum-exp of each row's scaled logits (-inf for a row with no visible
  *   key, whose output is 0).
  * Arithmetic: bf16 products with fp32 accumulation, fp32 online softmax, P rounded to
- * bf16 before the P.V product.  Errors: head counts or head_dim differing from the
- * cache's, head_dim not 64 or 128 -> INVALID_ARG / UNSUPPORTED. */
+ * bf16 before the P.V product.  A query tile's keys may be split over several workgroups,
+ * whose partial results are merged in a fixed order: outputs are deterministic for a given
+ * device.
+ * Memory: for CHUNK_CAUSAL and DENSE the library keeps a workspace per (device, stream),
+ * allocated (hipMalloc, with a device synchronisation) on the first call that needs more and
+ * kept until the process ends: per-tile counters (4 bytes per head and query tile) and
+ * partial results (two 135 KB slots per CU for head_dim 128).  Calls on one stream are ordered;
+ * calls that may run at the same time must use different streams.
+ * Errors: head counts or head_dim differing from the cache's, head_dim not 64 or 128 ->
+ * INVALID_ARG / UNSUPPORTED; more than 4096 query tiles in one call -> UNSUPPORTED (split the
+ * call by frames); allocation failure -> DEVICE. */
 int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
                         const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
                         float softmax_scale, vdit_tensor o, float* lse, void* stream);

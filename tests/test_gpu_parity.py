@@ -196,3 +196,59 @@ def test_deterministic():
     b = run_workload(w, inp)
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
     assert (device_plan_words(a["plan"]) == device_plan_words(b["plan"])).all()
+
+
+def test_workspace_reuse_across_shapes_and_streams():
+    """A call with many split tiles leaves partial results in the per-stream workspace; a
+    later call with more (head, query tile) pairs must still find all its per-tile counters
+    at zero and give the oracle's output, on the default stream and on a second stream."""
+    _print("workspace reuse")
+    first = get_workload("wan13b_chunk_h2")
+    run_workload(first, make_inputs(first))
+    w = get_workload("small_radial")
+    inp = make_inputs(w)
+    r = run_workload(w, inp)
+    o = r["o"].float().cpu().numpy()
+    ref = _oracle_rows(w, inp, range(w.heads), np.arange(w.n_q))
+    for h in range(w.heads):
+        compare(o[:, h], ref[h][0], what=f"after reuse, head {h}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # the session has no stream of its own: it uses the current one
+        o2 = r["session"].attend(r["q"], w.q_frames, w.q_t0, r["plan"])
+    torch.cuda.synchronize()
+    assert torch.equal(o2, r["o"])
+    again = run_workload(w, inp)["o"]
+    assert torch.equal(again, r["o"])
+
+
+def test_query_tile_without_keys():
+    """A plan row with no spans (possible in a hand-made plan) gives O = 0 and LSE = -inf
+    for that query tile; every other tile is unchanged."""
+    _print("query tile without keys")
+    w = get_workload("small_chunk_pad")
+    inp = make_inputs(w)
+    r = run_workload(w, inp)
+    p = device_plan_words(r["plan"]).copy()
+    nq, ns = int(p[4]), int(p[5])
+    qt = p[8:8 + 2 * nq].reshape(nq, 2)
+    rp = p[8 + 2 * nq:8 + 3 * nq + 1].copy()
+    sp = p[8 + 3 * nq + 1:].reshape(ns, 2)
+    drop = 1
+    keep = np.r_[0:rp[drop], rp[drop + 1]:ns]
+    rp2 = rp.copy()
+    rp2[drop + 1:] -= rp[drop + 1] - rp[drop]
+    hdr = p[:8].copy()
+    hdr[5] = len(keep)
+    words = np.concatenate([hdr, qt.ravel(), rp2, sp[keep].ravel()]).astype(np.int32)
+    plan2 = torch.from_numpy(words).to("cuda")
+    lse = torch.empty((w.heads, w.n_q), dtype=torch.float32, device="cuda")
+    o = r["session"].attend(r["q"], w.q_frames, w.q_t0, plan2, lse=lse)
+    torch.cuda.synchronize()
+    rows = slice(int(qt[drop, 0]), int(qt[drop, 0] + qt[drop, 1]))
+    assert (o[rows].float() == 0).all()
+    assert torch.isneginf(lse[:, rows]).all()
+    other = torch.ones(w.n_q, dtype=torch.bool, device="cuda")
+    other[rows] = False
+    assert torch.equal(o[other], r["o"][other])
+    assert torch.equal(lse[:, other], r["lse"][:, other])

@@ -413,8 +413,12 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
     a.heads = cache->heads;
     a.head_dim = cache->head_dim;
     a.n_qtiles = plan_qtile_count(g);
+    a.mask_kind = mask->kind;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     if (n == 0 || a.n_qtiles == 0) return ok();
+    if (a.n_qtiles > kAttnMaxQTiles)
+        return fail(VDIT_ERR_UNSUPPORTED, "%d query tiles in one call; at most %d (split the call by frames)",
+                    a.n_qtiles, kAttnMaxQTiles);
     return device_status(launch_attn_fwd(a, (hipStream_t)stream), "attention kernel");
 }
 

@@ -188,8 +188,11 @@ struct AttnLaunch {
     RopeDev rope;
     bool has_rope;
     int32_t hw, wf, t0, n_tokens, heads, head_dim, n_qtiles;
+    int32_t mask_kind;
     float scale_log2;
 };
+// Query tiles one attention call can hold (its unit table lives in LDS).
+constexpr int32_t kAttnMaxQTiles = 4096;
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t s);
 
 }  // namespace vdit
