@@ -26,6 +26,9 @@ METRIC = "attention ms/chunk and TFLOP/s on computed blocks; % of bf16 MFMA peak
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_rope3d_amd", "csrc", "vdit_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+# the attention kernel of the chunk-causal and dense workloads (one workgroup per CU, query
+# tiles paired into units); log-radial plans run attn_tile_kernel
+ATTN_KERNEL = "attn_unit_kernel"
 
 
 def parse():
@@ -106,8 +109,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
             raise SystemExit(f"no {counter} sample of a kernel matching {needle!r} in {path}")
         return vals
 
-    attn_fetch = per_kernel(fetch_csv, "FETCH_SIZE", "attn_fwd_kernel")
-    attn_write = per_kernel(write_csv, "WRITE_SIZE", "attn_fwd_kernel")
+    attn_fetch = per_kernel(fetch_csv, "FETCH_SIZE", ATTN_KERNEL)
+    attn_write = per_kernel(write_csv, "WRITE_SIZE", ATTN_KERNEL)
     # the calibration copy is the largest copy dispatch of the run
     copy_fetch = max(per_kernel(fetch_csv, "FETCH_SIZE", "copyBuffer"))
     copy_write = max(per_kernel(write_csv, "WRITE_SIZE", "copyBuffer"))
@@ -117,7 +120,7 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
     fetch_kib = sum(attn_fetch) / len(attn_fetch)
     write_kib = sum(attn_write) / len(attn_write)
     hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
-    out = {"kernel": "attn_fwd_kernel", "kernel_source_sha256": source_sha(ATTN_SRC),
+    out = {"kernel": ATTN_KERNEL, "kernel_source_sha256": source_sha(ATTN_SRC),
            "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
            "dispatches": [len(attn_fetch), len(attn_write)],
            "copy_calibration": {"bytes": copy_bytes, "fetch_kib": copy_fetch, "write_kib": copy_write,
