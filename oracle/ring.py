@@ -31,13 +31,17 @@ class RingCache:
         self.k = [None] * capacity  # per slot: [HW, H, D] float64, rotated
         self.v = [None] * capacity
 
+    def slot_of(self, t: int) -> int:
+        """Slot of global frame t."""
+        return t % self.capacity
+
     def append(self, k: np.ndarray, v: np.ndarray, frames: int, t0: int, dims, theta, rotate: bool = True):
         """Write `frames` frames starting at global frame t0 (k, v: [frames*HW, H, D])."""
         hw = self.tokens_per_frame
         assert frames <= self.capacity
         if k is None:  # slot bookkeeping only (plan tests need no data)
             for f in range(frames):
-                self.slot_frame[(t0 + f) % self.capacity] = t0 + f
+                self.slot_frame[self.slot_of(t0 + f)] = t0 + f
             return
         assert k.shape == (frames * hw, self.heads, self.head_dim) and v.shape == k.shape
         k = np.asarray(k, dtype=np.float64)
@@ -45,7 +49,7 @@ class RingCache:
             k = rope3d(k, token_positions(frames, self.frame_h, self.frame_w, t0), dims, theta)
         for f in range(frames):
             t = t0 + f
-            slot = t % self.capacity
+            slot = self.slot_of(t)
             self.slot_frame[slot] = t
             self.k[slot] = k[f * hw:(f + 1) * hw].copy()
             self.v[slot] = np.asarray(v[f * hw:(f + 1) * hw], dtype=np.float64).copy()
@@ -73,21 +77,10 @@ class RingCache:
         Returns (phys, t, s, k, v): physical index slot*frame_stride + s, global
         frame t, within-frame index s, keys [Nk, H, D] and values [Nk, H, D].
         """
-        hw = self.tokens_per_frame
-        phys, tt, ss, ks, vs = [], [], [], [], []
-        for slot in range(self.capacity):
-            t = self.slot_frame[slot]
-            if t < 0:
-                continue
-            s = np.arange(hw, dtype=np.int64)
-            phys.append(slot * frame_stride + s)
-            tt.append(np.full(hw, t, dtype=np.int64))
-            ss.append(s)
-            ks.append(self.k[slot])
-            vs.append(self.v[slot])
-        if not phys:
-            e = np.zeros(0, dtype=np.int64)
+        phys, tt, ss = self.key_layout(frame_stride)
+        full = [slot for slot in range(self.capacity) if self.slot_frame[slot] >= 0]
+        if not full:
             z = np.zeros((0, self.heads, self.head_dim))
-            return e, e, e, z, z
-        return (np.concatenate(phys), np.concatenate(tt), np.concatenate(ss),
-                np.concatenate(ks), np.concatenate(vs))
+            return phys, tt, ss, z, z
+        return (phys, tt, ss, np.concatenate([self.k[slot] for slot in full]),
+                np.concatenate([self.v[slot] for slot in full]))

@@ -1,0 +1,120 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each entry plants one plausible mistake in a copy of oracle/: a dropped term, a wrong
+sign, index or operand order, an off-by-one.  The pins of tests/test_oracle_pins.py
+(closed forms, library routines, hand-derived fixtures, brute force) must fail on every
+mutant; a mutant that passes them shows a part of the oracle that nothing external pins.
+The mutants run in parallel subprocesses, each in a scratch tree holding the mutated
+oracle, the seeded workloads and the pin tests.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (file under oracle/, original text, mutated text, what the mistake is)
+MUTATIONS = [
+    # token positions and RoPE
+    ("rope3d.py", "return np.stack([t0 + f, s // width, s % width], axis=1)",
+     "return np.stack([f, s // width, s % width], axis=1)", "local frame index instead of the global one"),
+    ("rope3d.py", "return np.stack([t0 + f, s // width, s % width], axis=1)",
+     "return np.stack([t0 + f, s % width, s // width], axis=1)", "h and w swapped"),
+    ("rope3d.py", "return np.power(float(theta), -2.0 * j / dim)",
+     "return np.power(float(theta), -1.0 * j / dim)", "wrong frequency exponent"),
+    ("rope3d.py", "out[:, :, offset:offset + d_a:2] = x_even * c - x_odd * s",
+     "out[:, :, offset:offset + d_a:2] = x_even * c + x_odd * s", "sign of the rotation"),
+    ("rope3d.py", "out[:, :, offset + 1:offset + d_a:2] = x_even * s + x_odd * c",
+     "out[:, :, offset + 1:offset + d_a:2] = x_odd * s + x_even * c", "operands of the odd channel swapped"),
+    ("rope3d.py", "offset += d_a", "offset += d_a // 2", "wrong group offset"),
+    ("rope3d.py", "for axis, d_a in enumerate(dims):",
+     "for axis, d_a in zip((2, 1, 0), dims):", "axis groups in the wrong order"),
+    # attention
+    ("attention.py", "s = (q @ k.T) * scale", "s = (q @ k.T)", "softmax scale dropped"),
+    ("attention.py", "s = np.where(allowed, s, -np.inf)", "s = np.where(allowed, s, 0.0)",
+     "masked logits kept at 0"),
+    ("attention.py", "o = (p @ v) / np.where(empty, 1.0, l)[:, None]", "o = (p @ v)",
+     "no normalisation by the row sum"),
+    ("attention.py", "lse = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, l)))",
+     "lse = np.where(empty, -np.inf, np.log(np.where(empty, 1.0, l)))", "row max missing from the LSE"),
+    # ring cache
+    ("ring.py", "return t % self.capacity", "return (t + 1) % self.capacity", "frame written to the wrong slot"),
+    ("ring.py", "self.slot_frame[self.slot_of(t0 + f)] = t0 + f",
+     "self.slot_frame[self.slot_of(t0 + f)] = f", "slot table records the local frame"),
+    ("ring.py", "k = rope3d(k, token_positions(frames, self.frame_h, self.frame_w, t0), dims, theta)",
+     "k = rope3d(k, token_positions(frames, self.frame_h, self.frame_w, 0), dims, theta)",
+     "keys rotated at local positions"),
+    ("ring.py", "phys.append(slot * frame_stride + s)", "phys.append(slot * hw + s)",
+     "physical index ignores the padded frame stride"),
+    # visibility rules
+    ("masks.py", "return (tokens_per_frame + 7) // 8 * 8", "return tokens_per_frame", "frame stride not padded"),
+    ("masks.py", "return math.ceil(Fraction(w0) / Fraction(2) ** (decay_log2 * d))",
+     "return math.floor(Fraction(w0) / Fraction(2) ** (decay_log2 * d))", "window rounded down"),
+    ("masks.py", "return math.ceil(Fraction(w0) / Fraction(2) ** (decay_log2 * d))",
+     "return math.ceil(Fraction(w0) / Fraction(2) ** (decay_log2 * (d + 1)))", "window decays one step early"),
+    ("masks.py", "(tk // mask.chunk_frames) <= (tq // mask.chunk_frames)",
+     "(tk // mask.chunk_frames) < (tq // mask.chunk_frames)", "a chunk does not see itself"),
+    ("masks.py", "(tk // mask.chunk_frames) <= (tq // mask.chunk_frames)", "tk <= tq",
+     "frame-causal instead of chunk-causal"),
+    ("masks.py", "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) <= window)",
+     "keep = np.broadcast_to(tile_gap, shape) <= window", "own frame limited to the window"),
+    ("masks.py", "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) <= window)",
+     "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) < window)", "window edge excluded"),
+    ("masks.py", "keep |= (d_b % mask.long_range_period) == 0", "pass", "long-range frames dropped"),
+    ("masks.py", "tile_gap = np.abs(sq // mask.tile - sk // mask.tile)",
+     "tile_gap = np.abs(sq - sk) // mask.tile", "tile distance taken on token indices"),
+    # plan
+    ("masks.py", "tiles.append((start + off, min(mask.tile, length - off)))",
+     "tiles.append((start + off, mask.tile))", "ragged last tile not shortened"),
+    ("masks.py", "cut = np.flatnonzero(np.diff(vis) != 1) + 1", "cut = np.flatnonzero(np.diff(vis) > 8) + 1",
+     "runs merged across small gaps"),
+    ("masks.py", "pairs & 0xFFFFFFFF, pairs >> 32]", "pairs & 0xFFFF, pairs >> 32]", "pair count truncated"),
+    ("masks.py", "        acc += len(sp)\n        words.append(acc)", "        words.append(acc)\n        acc += len(sp)",
+     "row pointers shifted by one tile"),
+]
+
+
+def _run_mutant(i, mutation):
+    fname, old, new, what = mutation
+    with tempfile.TemporaryDirectory(prefix="oracle_mutant_") as tmp:
+        for d in ("oracle", "workloads"):
+            shutil.copytree(os.path.join(ROOT, d), os.path.join(tmp, d),
+                            ignore=shutil.ignore_patterns("__pycache__"))
+        os.makedirs(os.path.join(tmp, "tests"))
+        for f in ("conftest.py", "test_oracle_pins.py"):
+            shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(tmp, "tests", f))
+        shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(tmp, "tests", "golden"))
+        path = os.path.join(tmp, "oracle", fname)
+        with open(path) as f:
+            src = f.read()
+        if src.count(old) < 1:
+            return i, "stale", f"{what}: text not found in oracle/{fname}"
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1", OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(tmp, "tests", "test_oracle_pins.py")],
+                           cwd=tmp, env=env, capture_output=True, text=True, timeout=900)
+        last = (r.stdout.strip().splitlines() or [""])[-1]
+        if r.returncode == 0:
+            return i, "survived", what
+        # killed means a pin failed, not that the mutant broke the test collection
+        return i, ("killed" if " failed" in last else "broken"), f"{what}: {last}"
+
+
+@pytest.mark.slow
+def test_every_planted_mistake_fails_a_pin():
+    workers = max(1, min(8, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(lambda a: _run_mutant(*a), enumerate(MUTATIONS)))
+    stale = [r for r in results if r[1] == "stale"]
+    broken = [r for r in results if r[1] == "broken"]
+    survived = [r for r in results if r[1] == "survived"]
+    assert not stale, f"mutations no longer apply: {stale}"
+    assert not broken, f"mutants that stop the pin tests from running: {broken}"
+    assert not survived, f"mutants the pins do not catch: {[r[2] for r in survived]}"

@@ -320,3 +320,53 @@ def test_query_tiles_units():
     assert (3120, 128) in tiles
     lr = query_tiles(MaskSpec("log_radial"), 2, 1560, 0)
     assert len(lr) == 26 and lr[12] == (1536, 24) and lr[13] == (1560, 128)
+
+
+def test_padded_plan_golden():
+    """Plans of 15-token frames (pitch 16): spans never merge across the padding."""
+    from oracle.masks import frame_stride_for, serialize_plan
+    for line in _read_golden("pad_plan.txt"):
+        cap, cf, appends, query, tiles = (p.strip() for p in line.split(";"))
+        mask = MaskSpec("chunk_causal", chunk_frames=int(cf))
+        ring = oracle.RingCache(int(cap), 3, 5, 1, 2)
+        for a in appends.split():
+            t0, f = (int(x) for x in a.split(":"))
+            ring.append(None, None, f, t0, (2, 0, 0), 1e4)
+        phys, kt, ks = ring.key_layout(frame_stride_for(15))
+        qt0, qf = (int(x) for x in query.split(":"))
+        pos = oracle.token_positions(qf, 3, 5, qt0)
+        q_s = np.arange(qf * 15) % 15
+        qtiles = query_tiles(mask, qf, 15, qt0)
+        spans = plan_from_mask(mask, pos[:, 0], q_s, qtiles, phys, kt, ks)
+        want_tiles = [t.strip() for t in tiles.split("|")]
+        assert len(qtiles) == len(want_tiles)
+        for (q0, ql), sp, wt in zip(qtiles, spans, want_tiles):
+            head, body = wt.split(":")
+            assert [q0, ql] == [int(x) for x in head.split()]
+            assert sp == [tuple(int(x) for x in s.split()) for s in body.split(",")]
+        words = serialize_plan(mask, qtiles, spans)
+        pairs = sum(ql * sum(kl for _, kl in sp) for (_, ql), sp in zip(qtiles, spans))
+        assert int(np.uint32(words[6])) + (int(np.uint32(words[7])) << 32) == pairs
+
+
+def test_plan_pair_count_words_beyond_32_bits():
+    """Header words 6, 7 hold the visible-pair count q_len * sum(k_len) in two 32-bit halves."""
+    from oracle.masks import serialize_plan
+    mask = MaskSpec("dense")
+    words = serialize_plan(mask, [(0, 128)], [[(0, 40_000_000), (40_000_008, 5)]])
+    pairs = 128 * (40_000_000 + 5)
+    assert pairs > 2 ** 32
+    assert int(np.uint32(words[6])) == pairs % 2 ** 32 and int(np.uint32(words[7])) == pairs // 2 ** 32
+    assert words[4] == 1 and words[5] == 2 and words[8:10].tolist() == [0, 128] and words[10:12].tolist() == [0, 2]
+
+
+def test_log_radial_own_frame_and_window_edge():
+    """Own frame (d = 0) fully visible whatever the window; at distance d the key tiles with
+    |tile gap| <= W(d) are kept and the next one is not (token-sized tiles, w0 = 1)."""
+    m = MaskSpec("log_radial", tile=1, radial_w0=1, radial_decay_log2=1, long_range_period=0)
+    sk = np.arange(40)[None, :]
+    own = allowed_mask(m, np.array([[4]]), np.array([[20]]), np.full((1, 40), 4), sk)
+    assert own.all()
+    m3 = MaskSpec("log_radial", tile=1, radial_w0=3, radial_decay_log2=0, long_range_period=0)  # W(d) = 3
+    near = allowed_mask(m3, np.array([[9]]), np.array([[20]]), np.full((1, 40), 10), sk)[0]
+    assert np.flatnonzero(near).tolist() == [17, 18, 19, 20, 21, 22, 23]
