@@ -71,9 +71,11 @@ __global__ void rope_inplace_kernel(RopeDev r, int32_t n, int32_t hw, int32_t wi
     store8<F32>(x, off, v);
 }
 
-// ---- KV append.  Block = 64 tokens x one head.  Keys: rotated (optional) and written
-// to k[h][phys][:].  Values: staged in LDS and written transposed to v[h][d][phys] so that
-// consecutive lanes write consecutive keys of one channel row.
+// ---- KV append.  Block = 64 tokens x one head.  Every thread issues all its global loads
+// before its first store (the compiler cannot move a load above a possibly aliasing store).
+// Keys: rotated (optional) and written to k[h][phys][:].  Values: staged in LDS by token
+// rows and written transposed to v[h][d][phys], consecutive lanes writing consecutive keys
+// of one channel row.
 constexpr int kAppendTok = 64;
 
 template <int D, bool F32>
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
                                                              uint16_t* kc, uint16_t* vt, int32_t* slot_frame,
                                                              int32_t frames) {
     constexpr int CH = D / 8;
-    constexpr int PITCH = D + 2;  // bf16 elements per LDS row, odd dword count per row
+    constexpr int PER = kAppendTok * CH / kThreads;  // chunks per thread
+    constexpr int PITCH = D + 2;                     // bf16 elements per LDS row, odd dword count per row
     __shared__ uint16_t sv[kAppendTok * PITCH];
     const int32_t h = blockIdx.y;
     const int32_t n0 = blockIdx.x * kAppendTok;
@@ -93,18 +96,26 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
 
     if (blockIdx.x == 0 && blockIdx.y == 0 && tid < frames) slot_frame[(t0 + tid) % capacity] = t0 + tid;
 
-    for (int c = tid; c < kAppendTok * CH; c += kThreads) {
-        int32_t lt = c / CH, ch = c % CH;
-        int32_t tok = n0 + lt;
+    float xk[PER][8], xv[PER][8];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int c = tid + i * kThreads;
+        const int32_t tok = n0 + c / CH, ch = c % CH;
+        if (tok < n) {
+            load8<F32>(k, (int64_t)tok * k_st + (int64_t)h * k_sh + ch * 8, xk[i]);
+            load8<F32>(v, (int64_t)tok * v_st + (int64_t)h * v_sh + ch * 8, xv[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int c = tid + i * kThreads;
+        const int32_t lt = c / CH, ch = c % CH, tok = n0 + lt;
         if (tok >= n) continue;
-        int32_t f = tok / hw, s = tok % hw;
-        int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
-        float x[8];
-        load8<F32>(k, (int64_t)tok * k_st + (int64_t)h * k_sh + ch * 8, x);
-        if (has_rope) rope_rotate8(r, ch * 4, t0 + f, s / width, s % width, x);
-        *reinterpret_cast<u32x4*>(kc + ((int64_t)h * kv_rows + phys) * D + ch * 8) = pack_bf16x8(x);
-        load8<F32>(v, (int64_t)tok * v_st + (int64_t)h * v_sh + ch * 8, x);
-        u32x4 pv = pack_bf16x8(x);
+        const int32_t f = tok / hw, s = tok % hw;
+        const int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
+        if (has_rope) rope_rotate8(r, ch * 4, t0 + f, s / width, s % width, xk[i]);
+        *reinterpret_cast<u32x4*>(kc + ((int64_t)h * kv_rows + phys) * D + ch * 8) = pack_bf16x8(xk[i]);
+        const u32x4 pv = pack_bf16x8(xv[i]);
         uint16_t* row = sv + lt * PITCH + ch * 8;
         const uint16_t* src = reinterpret_cast<const uint16_t*>(&pv);
 #pragma unroll
@@ -114,8 +125,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
     const int lane = tid & 63, wave = tid >> 6;
     const int32_t tok = n0 + lane;
     if (tok < n) {
-        int32_t f = tok / hw, s = tok % hw;
-        int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
+        const int32_t f = tok / hw, s = tok % hw;
+        const int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
         for (int d = wave; d < D; d += kThreads / 64) vt[((int64_t)h * D + d) * kv_rows + phys] = sv[lane * PITCH + d];
     }
 }
@@ -134,36 +145,32 @@ __global__ void kv_zero_pad_kernel(int32_t hw, int32_t frame_stride, int32_t t0,
     }
 }
 
-// ---- device plan builder: one workgroup.  Pass 1 counts spans per query tile, an
-// exclusive scan turns counts into row pointers, pass 2 writes the spans.  All integer,
-// so the words equal the host builder's.
-constexpr int kPlanThreads = 256;
+// ---- device plan builder: one wave.  Lane i of round r takes query tile 64 r + i: counts
+// its spans, a shuffle scan turns counts into row pointers, then it writes its spans.  All
+// integer, so the words equal the host builder's.
+constexpr int kPlanThreads = 64;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_build_kernel(PlanGeom g, const int32_t* slot_frame, int32_t nq,
                                                                   int32_t* plan) {
     __shared__ int32_t s_slot[1024];
-    __shared__ int32_t s_scan[kPlanThreads];
-    __shared__ long long s_pairs[kPlanThreads];
-    __shared__ int32_t s_carry;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const int32_t* sf = slot_frame;
     if (g.capacity <= 1024) {
-        for (int i = tid; i < g.capacity; i += kPlanThreads) s_slot[i] = slot_frame[i];
+        for (int i = lane; i < g.capacity; i += kPlanThreads) s_slot[i] = slot_frame[i];
         sf = s_slot;
     }
+    __syncthreads();
     int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
     int32_t* row_ptr = qtiles + 2 * nq;
     int32_t* spans = row_ptr + nq + 1;
-    if (tid == 0) s_carry = 0;
-    __syncthreads();
-
+    int32_t carry = 0;
     long long pairs = 0;
-    // pass 1 + scan, in chunks of kPlanThreads tiles
     for (int32_t base = 0; base < nq; base += kPlanThreads) {
-        int32_t i = base + tid;
+        const int32_t i = base + lane;
         int32_t cnt = 0;
+        QTile qt{0, 0, 0, 0, 0};
         if (i < nq) {
-            QTile qt = plan_qtile(g, i);
+            qt = plan_qtile(g, i);
             qtiles[2 * i] = qt.q_start;
             qtiles[2 * i + 1] = qt.q_len;
             long long keys = 0;
@@ -173,46 +180,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_build_kernel(PlanGeom g, co
             });
             pairs += keys * qt.q_len;
         }
-        s_scan[tid] = cnt;
-        __syncthreads();
+        int32_t incl = cnt;
+#pragma unroll
         for (int off = 1; off < kPlanThreads; off <<= 1) {
-            int32_t add = tid >= off ? s_scan[tid - off] : 0;
-            __syncthreads();
-            s_scan[tid] += add;
-            __syncthreads();
+            const int32_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
         }
-        if (i < nq) row_ptr[i + 1] = s_carry + s_scan[tid];
-        __syncthreads();
-        if (tid == kPlanThreads - 1) s_carry += s_scan[tid];
-        __syncthreads();
+        if (i < nq) {
+            row_ptr[i + 1] = carry + incl;
+            int32_t kk = carry + incl - cnt;
+            plan_tile_spans(g, sf, qt, [&](int32_t st, int32_t len) {
+                spans[2 * kk] = st;
+                spans[2 * kk + 1] = len;
+                ++kk;
+            });
+        }
+        carry += __shfl(incl, kPlanThreads - 1);
     }
-    if (tid == 0) row_ptr[0] = 0;
-    __threadfence_block();
-    __syncthreads();
-    // pass 2
-    for (int32_t i = tid; i < nq; i += kPlanThreads) {
-        QTile qt = plan_qtile(g, i);
-        int32_t k = i == 0 ? 0 : row_ptr[i];
-        plan_tile_spans(g, sf, qt, [&](int32_t s0, int32_t len) {
-            spans[2 * k] = s0;
-            spans[2 * k + 1] = len;
-            ++k;
-        });
-    }
-    s_pairs[tid] = pairs;
-    __syncthreads();
-    for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) s_pairs[tid] += s_pairs[tid + off];
-        __syncthreads();
-    }
-    if (tid == 0) {
-        unsigned long long tot = (unsigned long long)s_pairs[0];
+#pragma unroll
+    for (int off = kPlanThreads / 2; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
+    if (lane == 0) {
+        const unsigned long long tot = (unsigned long long)pairs;
+        row_ptr[0] = 0;
         plan[0] = (int32_t)VDIT_PLAN_MAGIC;
         plan[1] = VDIT_PLAN_VERSION;
         plan[2] = g.kind;
         plan[3] = g.tile;
         plan[4] = nq;
-        plan[5] = s_carry;
+        plan[5] = carry;
         plan[6] = (int32_t)(uint32_t)(tot & 0xFFFFFFFFull);
         plan[7] = (int32_t)(uint32_t)(tot >> 32);
     }
