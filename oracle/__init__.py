@@ -17,7 +17,10 @@ numpy, written for a reader to check against the pages by eye:
               built from the element mask (Wave Forcing page, block-causal
               attention; DynamicRad page, section 2, log-radial window and
               static-ratio mode);
-* attention - masked softmax attention (the exact result the method reaches).
+* attention - masked softmax attention (the exact result the method reaches);
+* dynamic   - the dynamic-threshold block plan (DynamicRad page, section 2, dual-mode
+              strategy, mode 2): pooled pre-softmax logits of (query tile, key tile)
+              pairs as importance proxies and an adaptive threshold.
 
 Pins (see tests/test_oracle_*.py): RoPE against the RoFormer rotary implementation in
 `transformers` and against invariants (norm, relative offset, per-axis

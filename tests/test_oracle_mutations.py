@@ -1,8 +1,9 @@
 """Mutation check of the oracle's pins (CPU only).
 
 Each entry plants one plausible mistake in a copy of oracle/: a dropped term, a wrong
-sign, index or operand order, an off-by-one.  The pins of tests/test_oracle_pins.py
-(closed forms, library routines, hand-derived fixtures, brute force) must fail on every
+sign, index or operand order, an off-by-one.  The pins of tests/test_oracle_pins.py and
+tests/test_oracle_dynamic.py (closed forms, library routines, hand-derived fixtures,
+brute force) must fail on every
 mutant; a mutant that passes them shows a part of the oracle that nothing external pins.
 The mutants run in parallel subprocesses, each in a scratch tree holding the mutated
 oracle, the seeded workloads and the pin tests.
@@ -17,6 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_dynamic.py")
 
 # (file under oracle/, original text, mutated text, what the mistake is)
 MUTATIONS = [
@@ -76,6 +78,14 @@ MUTATIONS = [
     ("masks.py", "pairs & 0xFFFFFFFF, pairs >> 32]", "pairs & 0xFFFF, pairs >> 32]", "pair count truncated"),
     ("masks.py", "        acc += len(sp)\n        words.append(acc)", "        words.append(acc)\n        acc += len(sp)",
      "row pointers shifted by one tile"),
+    # dynamic-threshold plan
+    ("dynamic.py", "qbar = np.stack([q_rot[q0:q0 + ql].mean(axis=0) for q0, ql in qtiles])",
+     "qbar = np.stack([q_rot[q0:q0 + ql].sum(axis=0) for q0, ql in qtiles])", "query tile summed, not averaged"),
+    ("dynamic.py", "(p - small[:, None]) >= (1.0 - tau) * (big - small)[:, None]",
+     "(p - small[:, None]) >= tau * (big - small)[:, None]", "threshold fraction inverted"),
+    ("dynamic.py", "c[i, j] = vis.all()", "c[i, j] = True", "candidates ignore the static rule"),
+    ("dynamic.py", "while end < n and k_t[order[end]] == t and k_s[order[end]] // tile == piece:",
+     "while end < n and k_t[order[end]] == t:", "key tiles are whole frames"),
 ]
 
 
@@ -86,7 +96,7 @@ def _run_mutant(i, mutation):
             shutil.copytree(os.path.join(ROOT, d), os.path.join(tmp, d),
                             ignore=shutil.ignore_patterns("__pycache__"))
         os.makedirs(os.path.join(tmp, "tests"))
-        for f in ("conftest.py", "test_oracle_pins.py"):
+        for f in ("conftest.py",) + PIN_FILES:
             shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(tmp, "tests", f))
         shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(tmp, "tests", "golden"))
         path = os.path.join(tmp, "oracle", fname)
@@ -97,8 +107,8 @@ def _run_mutant(i, mutation):
         with open(path, "w") as f:
             f.write(src.replace(old, new))
         env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1", OMP_NUM_THREADS="1")
-        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(tmp, "tests", "test_oracle_pins.py")],
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                           [os.path.join(tmp, "tests", f) for f in PIN_FILES],
                            cwd=tmp, env=env, capture_output=True, text=True, timeout=900)
         last = (r.stdout.strip().splitlines() or [""])[-1]
         if r.returncode == 0:
