@@ -5,7 +5,10 @@ A step is the whole hot path for one chunk: the chunk's K/V append into the ring
 attention forward with RoPE applied to Q while it is loaded.  Inputs are resident in HBM
 before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--dynamic-tau TAU] [--no-cpu-baseline]
+
+--dynamic-tau builds the content-adaptive plan (pooled tile logits, adaptive threshold)
+in place of the static one; the step then carries that plan's four launches.
 
 Prints one JSON line.  value = attention FLOP on computed blocks / step time (TFLOP/s);
 the attention kernel alone is timed with HIP events on its launch stream.
@@ -37,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan13b_chunk")
+    ap.add_argument("--dynamic-tau", type=float, default=None, metavar="TAU",
+                    help="build the dynamic-threshold plan (tau in [0, 1]) instead of the static one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until reached)")
@@ -164,17 +169,29 @@ def main():
         s.append(dev(hk), dev(hv), t0)
     q, k, v = dev(inputs["q"]), dev(inputs["k"]), dev(inputs["v"])
     o = torch.empty_like(q)
-    plan = torch.empty(s.plan_bound(w.q_frames, w.q_t0), dtype=torch.int32, device="cuda")
+    tau = args.dynamic_tau
+    if tau is None:
+        plan = torch.empty(s.plan_bound(w.q_frames, w.q_t0), dtype=torch.int32, device="cuda")
+        mask = s.mask
+    else:
+        plan = torch.empty(B.vdit_plan_dynamic_bound(s.mask, s.grid(w.q_frames), w.q_t0, s.cache),
+                           dtype=torch.int32, device="cuda")
+        mask = B.dynamic_mask(s.mask)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         s.append(k, v, w.q_t0)
-        s.plan(w.q_frames, w.q_t0, out=plan)
         if ev is not None:
             ev[0].record(stream)
-        s.attend(q, w.q_frames, w.q_t0, plan, o=o)
+        if tau is None:
+            s.plan(w.q_frames, w.q_t0, out=plan)
+        else:
+            s.plan_dynamic(q, w.q_frames, w.q_t0, tau, out=plan)
         if ev is not None:
             ev[1].record(stream)
+        s.attend(q, w.q_frames, w.q_t0, plan, o=o, mask=mask)
+        if ev is not None:
+            ev[2].record(stream)
 
     if args.calibrate_copy:
         n = args.calibrate_copy * 2 ** 20
@@ -191,8 +208,7 @@ def main():
     pairs = int(np.uint32(header[6])) + (int(np.uint32(header[7])) << 32)
     flop = 4.0 * w.head_dim * w.heads * pairs
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -202,8 +218,8 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in events]
-    attn_avg = sum(attn_ms) / len(attn_ms)
+    attn_avg = sum(b.elapsed_time(c) for _, b, c in events) / args.steps
+    plan_avg = sum(a.elapsed_time(b) for a, b, _ in events) / args.steps
     attn_tflops = flop / (attn_avg * 1e-3) / 1e12
 
     traffic = traffic_per_launch()
@@ -221,9 +237,11 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic",
         "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
-                   "q_tokens": w.n_q, "kv_tokens": int(pairs // max(w.n_q, 1)) if m.kind != "log_radial" else None,
+                   "q_tokens": w.n_q, "kv_tokens": int(pairs // max(w.n_q, 1)) if m.kind != "log_radial" and tau is None else None,
+                   "mean_keys_per_query": round(pairs / max(w.n_q, 1), 1),
                    "frame": f"{w.frame_h}x{w.frame_w}", "q_t0": w.q_t0, "mask": m.kind,
-                   "computed_block_flop": flop},
+                   "computed_block_flop": flop, "plan": "static" if tau is None else f"dynamic tau={tau}"},
+        "plan_ms_per_chunk": round(plan_avg, 4),
         "attn_ms_per_chunk": round(attn_avg, 4),
         "attn_tflops": round(attn_tflops, 2),
         "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),

@@ -51,6 +51,9 @@ extern "C" {
 #define VDIT_MASK_DENSE 0
 #define VDIT_MASK_CHUNK_CAUSAL 1
 #define VDIT_MASK_LOG_RADIAL 2
+/* OR-ed into the kind of the mask given to vdit_block_attn_fwd when its plan comes from
+ * vdit_plan_dynamic (also set in such a plan's header kind word) */
+#define VDIT_MASK_FLAG_DYNAMIC 0x100
 
 /* where a plan or position list is produced */
 #define VDIT_WHERE_HOST 0
@@ -201,6 +204,36 @@ int vdit_plan_bound(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, c
 int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
                    int32_t where, int32_t* plan_out, size_t cap_words, size_t* used_words, void* stream);
 
+/* ---- dynamic-threshold block plan: "DynamicRad: Content-Adaptive Sparse Attention for
+ * Long Video Diffusion", section 2, dual-mode strategy, mode 2 (pre-softmax attention logits
+ * as importance proxies, an adaptive threshold inside the static rule's candidates).
+ * Key tiles: the `tile`-token pieces of each cache slot (the last piece of a frame ragged),
+ * numbered j = slot * ceil(tokens_per_frame / tile) + piece.  Proxy of query tile i and key
+ * tile j: scale * sum over heads of <mean rotated query of the tile, mean cached key of the
+ * tile> (the mean pre-softmax logit of the tile pair summed over heads; one plan serves all
+ * heads).  Candidates: the key tiles `base` (a static rule) lets the query tile see.  Kept:
+ * candidates with proxy p, p - m >= (1 - tau) * (M - m), M and m the largest and smallest
+ * candidate proxies of the query tile (tau = 1 keeps every candidate, tau = 0 the best).
+ * The plan has the usual words (query tiles of `base`, maximal runs of kept keys), its
+ * header kind is base->kind | VDIT_MASK_FLAG_DYNAMIC; attention on it takes a mask whose
+ * kind has that flag.
+ * q, rope: as for vdit_block_attn_fwd (the proxies use fp32 rotated queries).
+ * plan_dev: device, cap_words >= vdit_plan_dynamic_bound.  proxies_dev: NULL or device fp32
+ * [n_qtiles][capacity * ceil(tokens_per_frame / tile)] (written; empty slots give 0).
+ * Memory: a workspace per (device, stream) for the pooled tiles and proxies, allocated on the
+ * first call that needs more (hipMalloc) and kept until the process ends.
+ * Errors: as vdit_plan_mask and vdit_block_attn_fwd; tau outside [0, 1] -> INVALID_ARG;
+ *   more than 4096 key tiles (capacity * ceil(tokens_per_frame / tile)) -> UNSUPPORTED. */
+typedef struct {
+    float tau;
+    float softmax_scale; /* scale of the proxy logits; <= 0 selects 1/sqrt(head_dim) */
+} vdit_dynamic_cfg;
+int vdit_plan_dynamic_bound(const vdit_mask_cfg* base, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
+                            size_t* max_words);
+int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vdit_tensor q, const vdit_rope_cfg* rope,
+                      vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache, int32_t* plan_dev, size_t cap_words,
+                      float* proxies_dev, void* stream);
+
 /* ---- attention forward: the full spatiotemporal softmax attention of "DynamicRad ..."
  * section 1 and "Accelerating Video Generation Inference ..." section 1, restricted to
  * the visible keys of the plan, as a tiled (FlashAttention-style) pass that skips the
@@ -208,7 +241,9 @@ int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, co
  * q: [frames*height*width][heads][head_dim] bf16 or fp32 (device); if rope != NULL the
  *   queries are rotated at (q_t0 + f, h, w) while they are loaded (fp32 arithmetic, one
  *   rounding to bf16); with rope == NULL they are used as given (rounded to bf16).
- * plan_dev: device plan built for this rule, grid, q_t0 and the cache's current slots.
+ * plan_dev: device plan built for this rule, grid, q_t0 and the cache's current slots
+ *   (by vdit_plan_mask, or by vdit_plan_dynamic with base = this rule, in which case
+ *   mask->kind carries VDIT_MASK_FLAG_DYNAMIC).
  * softmax_scale <= 0 selects 1/sqrt(head_dim).
  * o: same shape as q, bf16 or fp32 (device).  lse: NULL or device fp32 [heads][tokens],
  *   natural-log log-sum-exp of each row's scaled logits (-inf for a row with no visible
@@ -217,7 +252,7 @@ int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, co
  * bf16 before the P.V product.  A query tile's keys may be split over several workgroups,
  * whose partial results are merged in a fixed order: outputs are deterministic for a given
  * device.
- * Memory: for CHUNK_CAUSAL and DENSE the library keeps a workspace per (device, stream),
+ * Memory: for CHUNK_CAUSAL and DENSE static plans the library keeps a workspace per (device, stream),
  * allocated (hipMalloc, with a device synchronisation) on the first call that needs more and
  * kept until the process ends: per-tile counters (4 bytes per head and query tile) and
  * partial results (two 135 KB slots per CU for head_dim 128).  Calls on one stream are ordered;

@@ -227,3 +227,36 @@ def test_attention_errors(L):
     rope.table = fake
     assert L.vdit_block_attn_fwd(t, ctypes.byref(rope), g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
                                  None, None) == B.VDIT_ERR_INVALID_ARG
+
+
+def test_dynamic_plan_errors(L):
+    """vdit_plan_dynamic / _bound validate before any device work: the bound counts every key
+    tile of every slot as its own run; tau outside [0, 1], a missing config, a short buffer and
+    more than 4096 key tiles are refused."""
+    slots = np.array([0, 1, 2], np.int32)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    desc = B.VditKVCache(fake, fake, fake, slots.ctypes.data, 3, 24, 2, 64)
+    m = B.mask_cfg("chunk_causal", 1)
+    g = B.grid(3, 4, 6)
+    t = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    words = ctypes.c_size_t(0)
+    assert L.vdit_plan_dynamic_bound(ctypes.byref(m), g, 0, ctypes.byref(desc), ctypes.byref(words)) == 0
+    nq, nk = 3, 3  # one 24-token tile per frame; 3 slots of one key tile each
+    assert words.value == 8 + 2 * nq + nq + 1 + 2 * nq * nk
+    for tau in (-0.1, 1.5, float("nan")):
+        dyn = B.VditDynamicCfg(tau, 0.0)
+        assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(desc), fake,
+                                   words.value, None, None) == B.VDIT_ERR_INVALID_ARG
+    dyn = B.VditDynamicCfg(0.5, 0.0)
+    assert L.vdit_plan_dynamic(ctypes.byref(m), None, t, None, g, 0, ctypes.byref(desc), fake, words.value, None,
+                               None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(desc), fake,
+                               words.value - 1, None, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    many = np.full(4097, -1, np.int32)  # 4097 slots of one key tile each
+    deep = B.VditKVCache(fake, fake, fake, many.ctypes.data, 4097, 24, 2, 64)
+    assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(deep), fake,
+                               1 << 20, None, None) == B.VDIT_ERR_UNSUPPORTED
+    # attention with the flag on a kind that does not exist
+    bad = B.dynamic_mask(B.mask_cfg(7))
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(bad), fake, 0.0, t, None,
+                                 None) == B.VDIT_ERR_INVALID_ARG

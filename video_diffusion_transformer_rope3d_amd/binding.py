@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvdit.so"
 VDIT_OK, VDIT_ERR_INVALID_ARG, VDIT_ERR_BUFFER_TOO_SMALL, VDIT_ERR_UNSUPPORTED, VDIT_ERR_DEVICE = range(5)
 VDIT_DTYPE_BF16, VDIT_DTYPE_FP32 = 0, 1
 VDIT_MASK_DENSE, VDIT_MASK_CHUNK_CAUSAL, VDIT_MASK_LOG_RADIAL = 0, 1, 2
+VDIT_MASK_FLAG_DYNAMIC = 0x100
 VDIT_WHERE_HOST, VDIT_WHERE_DEVICE = 0, 1
 VDIT_PLAN_MAGIC = 0x54494456
 MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, "log_radial": VDIT_MASK_LOG_RADIAL}
@@ -24,7 +25,8 @@ MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, 
 EXPORTS = (
     "vdit_abi_version", "vdit_last_error", "vdit_status_string", "vdit_token_positions",
     "vdit_rope_table_build", "vdit_rope3d_qk", "vdit_kv_cache_bytes", "vdit_kv_cache_reset",
-    "vdit_kv_append", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_block_attn_fwd",
+    "vdit_kv_append", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
+    "vdit_plan_dynamic", "vdit_block_attn_fwd",
 )
 
 
@@ -54,6 +56,10 @@ class VditMaskCfg(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("chunk_frames", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("radial_w0", ctypes.c_int32), ("radial_decay_log2", ctypes.c_int32),
                 ("long_range_period", ctypes.c_int32)]
+
+
+class VditDynamicCfg(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
 
 
 class VditError(RuntimeError):
@@ -90,6 +96,11 @@ def lib():
             "vdit_plan_bound": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(VditKVCache), pS]),
             "vdit_plan_mask": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(VditKVCache), I32,
                                      P, SZ, pS, P]),
+            "vdit_plan_dynamic_bound": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32,
+                                              ctypes.POINTER(VditKVCache), pS]),
+            "vdit_plan_dynamic": (I32, [ctypes.POINTER(VditMaskCfg), ctypes.POINTER(VditDynamicCfg), VditTensor,
+                                        ctypes.POINTER(VditRopeCfg), VditGrid, I32, ctypes.POINTER(VditKVCache),
+                                        P, SZ, P, P]),
             "vdit_block_attn_fwd": (I32, [VditTensor, ctypes.POINTER(VditRopeCfg), VditGrid, I32,
                                           ctypes.POINTER(VditKVCache), ctypes.POINTER(VditMaskCfg), P,
                                           ctypes.c_float, VditTensor, P, P]),
@@ -261,6 +272,34 @@ def vdit_plan_mask(mask: VditMaskCfg, g: VditGrid, q_t0: int, cache: KVCache, wh
     _check(lib().vdit_plan_mask(ctypes.byref(mask), g, q_t0, ctypes.byref(cache.desc), where,
                                 buf.data_ptr(), buf.numel(), ctypes.byref(used), _stream(stream)))
     return buf
+
+
+def vdit_plan_dynamic_bound(base: VditMaskCfg, g: VditGrid, q_t0: int, cache: KVCache) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vdit_plan_dynamic_bound(ctypes.byref(base), g, q_t0, ctypes.byref(cache.desc), ctypes.byref(n)))
+    return n.value
+
+
+def vdit_plan_dynamic(base: VditMaskCfg, tau: float, q, rope, g: VditGrid, q_t0: int, cache: KVCache,
+                      softmax_scale: float = 0.0, out=None, proxies=None, stream=None):
+    """Dynamic-threshold plan on the device (int32 tensor of the bound size; `out` reused if
+    given); `proxies`: optional fp32 device tensor [n_qtiles][key tiles] that receives them."""
+    import torch
+    bound = vdit_plan_dynamic_bound(base, g, q_t0, cache)
+    buf = torch.empty(bound, dtype=torch.int32, device="cuda") if out is None else out
+    dyn = VditDynamicCfg(tau, softmax_scale)
+    rp = ctypes.byref(rope.cfg) if rope is not None else None
+    _check(lib().vdit_plan_dynamic(ctypes.byref(base), ctypes.byref(dyn), tensor(q), rp, g, q_t0,
+                                   ctypes.byref(cache.desc), buf.data_ptr(), buf.numel(),
+                                   None if proxies is None else proxies.data_ptr(), _stream(stream)))
+    return buf
+
+
+def dynamic_mask(base: VditMaskCfg) -> VditMaskCfg:
+    """The mask to give vdit_block_attn_fwd for a plan made by vdit_plan_dynamic from `base`."""
+    m = VditMaskCfg.from_buffer_copy(base)
+    m.kind = base.kind | VDIT_MASK_FLAG_DYNAMIC
+    return m
 
 
 def vdit_block_attn_fwd(q, rope, g: VditGrid, q_t0: int, cache: KVCache, mask: VditMaskCfg, plan_dev,

@@ -379,9 +379,75 @@ int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, co
     return ok();
 }
 
+int vdit_plan_dynamic_bound(const vdit_mask_cfg* base, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
+                            size_t* max_words) {
+    int st = check_plan_args(base, q_grid, q_t0, cache);
+    if (st) return st;
+    if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
+    if (!max_words) return fail(VDIT_ERR_INVALID_ARG, "max_words is NULL");
+    PlanGeom g = make_geom(base, q_grid, q_t0, cache);
+    // every key tile of every slot may form its own run
+    *max_words = plan_bound_words(plan_qtile_count(g), cache->capacity * ceil_div(g.hw, g.tile));
+    return ok();
+}
+
+int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vdit_tensor q, const vdit_rope_cfg* rope,
+                      vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache, int32_t* plan_dev, size_t cap_words,
+                      float* proxies_dev, void* stream) {
+    int st = check_plan_args(base, q_grid, q_t0, cache);
+    if (st) return st;
+    if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
+    if (!cache->k || !cache->v || !cache->slot_frame_dev) return fail(VDIT_ERR_INVALID_ARG, "cache buffers must be set");
+    if (!dyn) return fail(VDIT_ERR_INVALID_ARG, "dynamic cfg is NULL");
+    if (!(dyn->tau >= 0.f && dyn->tau <= 1.f)) return fail(VDIT_ERR_INVALID_ARG, "tau %g outside [0, 1]", dyn->tau);
+    if (!plan_dev) return fail(VDIT_ERR_INVALID_ARG, "plan is NULL");
+    int32_t n = q_grid.frames * q_grid.height * q_grid.width;
+    if ((st = check_tensor(q, "q", n, cache->heads, cache->head_dim))) return st;
+    PlanGeom g = make_geom(base, q_grid, q_t0, cache);
+    const int32_t nq = plan_qtile_count(g);
+    if ((int64_t)cache->capacity * ceil_div(g.hw, g.tile) > kDynMaxKeyTiles)
+        return fail(VDIT_ERR_UNSUPPORTED, "%d key tiles in the cache; the dynamic plan weighs at most %d",
+                    cache->capacity * ceil_div(g.hw, g.tile), kDynMaxKeyTiles);
+    const size_t need = plan_bound_words(nq, cache->capacity * ceil_div(g.hw, g.tile));
+    if (cap_words < need)
+        return fail(VDIT_ERR_BUFFER_TOO_SMALL, "plan buffer holds %zu words, the bound is %zu", cap_words, need);
+    DynLaunch a{};
+    if (rope) {
+        if ((st = check_rope_use(rope, cache->head_dim, q_grid, q_t0))) return st;
+        a.rope = rope_dev(rope);
+        a.has_rope = true;
+    }
+    float scale = dyn->softmax_scale > 0.f ? dyn->softmax_scale : 1.0f / sqrtf((float)cache->head_dim);
+    a.geom = g;
+    a.q = q;
+    a.width = q_grid.width;
+    a.heads = cache->heads;
+    a.head_dim = cache->head_dim;
+    a.n_qtiles = nq;
+    a.slot_frame = cache->slot_frame_dev;
+    a.kc = cache->k;
+    a.kv_rows = (int64_t)cache->capacity * frame_stride_of(cache->tokens_per_frame);
+    a.scale = scale;
+    a.keep_frac = 1.0f - dyn->tau;
+    a.proxies = proxies_dev;
+    a.plan = plan_dev;
+    if (n == 0 || nq == 0) return ok();
+    return device_status(launch_plan_dynamic(a, (hipStream_t)stream), "dynamic plan kernels");
+}
+
 int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
-                        const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
+                        const vdit_kv_cache* cache, const vdit_mask_cfg* mask_in, const int32_t* plan_dev,
                         float softmax_scale, vdit_tensor o, float* lse, void* stream) {
+    // a plan from vdit_plan_dynamic is marked in the kind; the geometry is the base rule's
+    vdit_mask_cfg mask_base{};
+    const vdit_mask_cfg* mask = mask_in;
+    bool unpaired = false;
+    if (mask_in && (mask_in->kind & VDIT_MASK_FLAG_DYNAMIC)) {
+        mask_base = *mask_in;
+        mask_base.kind &= ~VDIT_MASK_FLAG_DYNAMIC;
+        mask = &mask_base;
+        unpaired = true;
+    }
     int st = check_plan_args(mask, q_grid, q_t0, cache);
     if (st) return st;
     if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
@@ -414,6 +480,7 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
     a.head_dim = cache->head_dim;
     a.n_qtiles = plan_qtile_count(g);
     a.mask_kind = mask->kind;
+    a.unpaired = unpaired;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     if (n == 0 || a.n_qtiles == 0) return ok();
     if (a.n_qtiles > kAttnMaxQTiles)

@@ -189,10 +189,28 @@ struct AttnLaunch {
     bool has_rope;
     int32_t hw, wf, t0, n_tokens, heads, head_dim, n_qtiles;
     int32_t mask_kind;
+    bool unpaired;  // plan from vdit_plan_dynamic: neighbouring tiles do not share span lists
     float scale_log2;
 };
+struct DynLaunch {
+    PlanGeom geom;  // static rule of the call (candidates and query tiles)
+    vdit_tensor q;
+    RopeDev rope;
+    bool has_rope;
+    int32_t width, heads, head_dim, n_qtiles;
+    const int32_t* slot_frame;
+    const void* kc;
+    int64_t kv_rows;
+    float scale, keep_frac;  // keep_frac = 1 - tau
+    float* proxies;          // optional [n_qtiles][capacity * tiles per frame]
+    int32_t* plan;
+};
+hipError_t launch_plan_dynamic(const DynLaunch& a, hipStream_t s);
+
 // Query tiles one attention call can hold (its unit table lives in LDS).
 constexpr int32_t kAttnMaxQTiles = 4096;
+// key tiles (cache slots x tiles per frame) one dynamic plan may weigh
+constexpr int32_t kDynMaxKeyTiles = 4096;
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t s);
 
 }  // namespace vdit

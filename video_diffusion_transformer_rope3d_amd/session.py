@@ -40,6 +40,13 @@ class AttentionSession:
     def plan_bound(self, q_frames, q_t0):
         return B.vdit_plan_bound(self.mask, self.grid(q_frames), q_t0, self.cache)
 
-    def attend(self, q, q_frames, q_t0, plan, o=None, lse=None, rotate=True, softmax_scale=0.0):
+    def attend(self, q, q_frames, q_t0, plan, o=None, lse=None, rotate=True, softmax_scale=0.0, mask=None):
+        """`mask`: the session's rule by default; B.dynamic_mask(session.mask) for a plan from
+        plan_dynamic."""
         return B.vdit_block_attn_fwd(q, self.rope if rotate else None, self.grid(q_frames), q_t0, self.cache,
-                                     self.mask, plan, softmax_scale, o, lse, self.stream)
+                                     self.mask if mask is None else mask, plan, softmax_scale, o, lse, self.stream)
+
+    def plan_dynamic(self, q, q_frames, q_t0, tau, out=None, proxies=None, rotate=True, softmax_scale=0.0):
+        """Dynamic-threshold plan of the session's rule on the device."""
+        return B.vdit_plan_dynamic(self.mask, tau, q, self.rope if rotate else None, self.grid(q_frames), q_t0,
+                                   self.cache, softmax_scale, out, proxies, self.stream)
