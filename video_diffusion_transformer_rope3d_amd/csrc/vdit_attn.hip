@@ -176,31 +176,73 @@ __device__ inline long long uniform64(long long x) {
     return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
-// A plan word read by the whole workgroup.  The kernel stores to global memory, so the
-// compiler cannot prove plan words unchanged and reads them with vector loads; the explicit
-// broadcast keeps values that feed buffer offsets in scalar registers (no waterfall loops).
-__device__ inline int plan_word(const int32_t* p) { return __builtin_amdgcn_readfirstlane(*p); }
+// A plan word read by the whole workgroup.  The plan does not change while a kernel runs,
+// so it is read through the constant address space: uniform addresses become scalar loads
+// served by the scalar cache (eight spans per line) instead of vector loads with the full
+// L2 latency on the path to the next DMA.  The broadcast keeps the value in a scalar
+// register whatever load the compiler picks (no waterfall loops on buffer offsets).
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+__device__ inline int plan_word(const int32_t* p) {
+    return __builtin_amdgcn_readfirstlane(*(const const_i32_t*)p);
+}
 
 // Q rows of one wave (this lane's row), RoPE applied at the global position while loading.
+// All row loads are issued first, then the table loads of half the chunks at a time (a
+// bound on live registers), so the segment start waits for a few round trips instead of
+// one per chunk.
 template <int D, bool QF32>
 __device__ __forceinline__ void load_q_rows(const AttnArgs& a, int h, int row, int g, bf16x8 (&qreg)[D / 16]) {
+    constexpr int KS = D / 16, HALF = KS / 2;
+    using Raw = std::conditional_t<QF32, float4, u32x4>;
+    constexpr int PER = QF32 ? 2 : 1;  // 16-byte loads per chunk of 8 channels
     const int f = row / a.hw, s = row % a.hw;
     const int pt = a.t0 + f, ph = s / a.wf, pw = s % a.wf;
     const int64_t qoff = (int64_t)row * a.q_st + (int64_t)h * a.q_sh;
+    Raw raw[KS][PER];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         const int d0 = ks * 16 + g * 8;
-        float x[8];
         if constexpr (QF32) {
             const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff + d0);
-            float4 u = p[0], v = p[1];
+            raw[ks][0] = p[0];
+            raw[ks][1] = p[1];
+        } else {
+            raw[ks][0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qoff + d0);
+        }
+    }
+    auto unpack = [&](int ks, float (&x)[8]) {
+        if constexpr (QF32) {
+            const float4 u = raw[ks][0], v = raw[ks][1];
             x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
             x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
         } else {
-            unpack_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qoff + d0), x);
+            unpack_bf16x8(raw[ks][0], x);
         }
-        if (a.has_rope) rope_rotate8(a.rope, d0 / 2, pt, ph, pw, x);
-        qreg[ks] = __builtin_bit_cast(bf16x8, pack_bf16x8(x));
+    };
+    // The table choice of a pair depends only on the lane; left visible, it is hoisted out of
+    // the segment loop and its pointers stay live through the key loop (spills).
+    int g4 = g * 4;
+    asm volatile("" : "+v"(g4));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        float2 cs[HALF][4];
+        if (a.has_rope) {
+#pragma unroll
+            for (int i = 0; i < HALF; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs[i][e] = rope_cs(a.rope, (hf * HALF + i) * 8 + g4 + e, pt, ph, pw);
+        }
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            const int ks = hf * HALF + i;
+            float x[8];
+            unpack(ks, x);
+            if (a.has_rope) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rope_apply(cs[i][e], x[2 * e], x[2 * e + 1]);
+            }
+            qreg[ks] = __builtin_bit_cast(bf16x8, pack_bf16x8(x));
+        }
     }
 }
 

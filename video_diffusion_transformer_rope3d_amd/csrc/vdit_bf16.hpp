@@ -42,22 +42,30 @@ __device__ inline void unpack_bf16x8(u32x4 u, float x[8]) {
 // of width d turns by p * theta^(-2j/d), read from the precomputed (cos, sin) tables
 // ("Accelerating Video Generation Inference ...", section 2.C, precomputed RoPE;
 // "Timeripple ...", Metodologia 1, channel groups per axis).
+// (cos, sin) of channel pair p at position (t, h, w): the pair's axis table, row = the
+// position on that axis.  Branch-free (selects), so that the loads of several pairs can be
+// issued together.
+__device__ inline float2 rope_cs(const RopeDev& r, int32_t p, int32_t t, int32_t h, int32_t w) {
+    const bool in_t = p < r.pairs_t, in_h = p < r.pairs_t + r.pairs_h;
+    const float2* tab = in_t ? r.tab_t : (in_h ? r.tab_h : r.tab_w);
+    const int32_t coord = in_t ? t : (in_h ? h : w);
+    const int32_t pitch = in_t ? r.pairs_t : (in_h ? r.pairs_h : r.pairs_w);
+    const int32_t col = in_t ? p : (in_h ? p - r.pairs_t : p - r.pairs_t - r.pairs_h);
+    return tab[(int64_t)coord * pitch + col];
+}
+
+__device__ inline void rope_apply(float2 cs, float& x0, float& x1) {
+    const float a = x0, b = x1;
+    x0 = a * cs.x - b * cs.y;
+    x1 = a * cs.y + b * cs.x;
+}
+
 __device__ inline void rope_rotate8(const RopeDev& r, int32_t pair0, int32_t t, int32_t h, int32_t w, float x[8]) {
+    float2 cs[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        int32_t p = pair0 + e;
-        float2 cs;
-        if (p < r.pairs_t) {
-            cs = r.tab_t[(int64_t)t * r.pairs_t + p];
-        } else if (p < r.pairs_t + r.pairs_h) {
-            cs = r.tab_h[h * r.pairs_h + (p - r.pairs_t)];
-        } else {
-            cs = r.tab_w[w * r.pairs_w + (p - r.pairs_t - r.pairs_h)];
-        }
-        float x0 = x[2 * e], x1 = x[2 * e + 1];
-        x[2 * e] = x0 * cs.x - x1 * cs.y;
-        x[2 * e + 1] = x0 * cs.y + x1 * cs.x;
-    }
+    for (int e = 0; e < 4; ++e) cs[e] = rope_cs(r, pair0 + e, t, h, w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rope_apply(cs[e], x[2 * e], x[2 * e + 1]);
 }
 
 }  // namespace vdit
