@@ -17,17 +17,24 @@ W(d) = ceil(w0 * gamma**d) with gamma = 2**-decay_log2 at frame distance d; a ke
 tile is kept when its tile index differs from the query tile's by at most W(d);
 d = 0 and (if the period lambda > 0) every d that is a multiple of lambda keep the
 whole frame; the rule is symmetric in time (a full clip, no causality).
+
+Streaming log-radial ("log_radial_causal"): the same window at the global frame distance,
+restricted to block-causal visibility (a key frame's chunk is not after the query's),
+for chunk-wise generation against the ring cache (the Wave Forcing page's block-causal
+chunks with the DynamicRad window; the global time index of the Causal-RoPE SP page makes
+frame distances between a chunk and cached frames well defined).
 """
 from __future__ import annotations
 
 import math
+from dataclasses import replace
 from fractions import Fraction
 
 import numpy as np
 
 PLAN_MAGIC = 0x54494456  # bytes 'V','D','I','T' little-endian
 PLAN_VERSION = 1
-KIND_CODE = {"dense": 0, "chunk_causal": 1, "log_radial": 2}
+KIND_CODE = {"dense": 0, "chunk_causal": 1, "log_radial": 2, "log_radial_causal": 3}
 
 
 def frame_stride_for(tokens_per_frame: int) -> int:
@@ -49,6 +56,10 @@ def allowed_mask(mask, tq, sq, tk, sk) -> np.ndarray:
         return np.ones(shape, dtype=bool)
     if mask.kind == "chunk_causal":
         return np.broadcast_to((tk // mask.chunk_frames) <= (tq // mask.chunk_frames), shape).copy()
+    if mask.kind == "log_radial_causal":
+        radial = allowed_mask(replace(mask, kind="log_radial"), tq, sq, tk, sk)
+        causal = allowed_mask(replace(mask, kind="chunk_causal"), tq, sq, tk, sk)
+        return radial & causal
     if mask.kind == "log_radial":
         d = np.abs(tq - tk)
         d_b = np.broadcast_to(d, shape)
@@ -83,7 +94,7 @@ def query_tiles(mask, frames: int, tokens_per_frame: int, t0: int):
                 g += 1
             units.append((f * tokens_per_frame, (g - f) * tokens_per_frame))
             f = g
-    elif mask.kind == "log_radial":
+    elif mask.kind in ("log_radial", "log_radial_causal"):
         units = [(f * tokens_per_frame, tokens_per_frame) for f in range(frames)]
     else:
         raise ValueError(mask.kind)

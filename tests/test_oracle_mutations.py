@@ -68,6 +68,12 @@ MUTATIONS = [
     ("masks.py", "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) <= window)",
      "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) < window)", "window edge excluded"),
     ("masks.py", "keep |= (d_b % mask.long_range_period) == 0", "pass", "long-range frames dropped"),
+    ("masks.py", "        return radial & causal", "        return radial",
+     "streaming log-radial sees later chunks"),
+    ("masks.py", "        return radial & causal", "        return radial & causal & (np.asarray(tk) <= np.asarray(tq))",
+     "streaming log-radial cut at the frame instead of the chunk"),
+    ("masks.py", 'elif mask.kind in ("log_radial", "log_radial_causal"):', 'elif mask.kind == "log_radial":',
+     "streaming log-radial query tiles not per frame"),
     ("masks.py", "tile_gap = np.abs(sq // mask.tile - sk // mask.tile)",
      "tile_gap = np.abs(sq - sk) // mask.tile", "tile distance taken on token indices"),
     # plan

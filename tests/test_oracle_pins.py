@@ -370,3 +370,46 @@ def test_log_radial_own_frame_and_window_edge():
     m3 = MaskSpec("log_radial", tile=1, radial_w0=3, radial_decay_log2=0, long_range_period=0)  # W(d) = 3
     near = allowed_mask(m3, np.array([[9]]), np.array([[20]]), np.full((1, 40), 10), sk)[0]
     assert np.flatnonzero(near).tolist() == [17, 18, 19, 20, 21, 22, 23]
+
+
+def test_stream_radial_plan_golden():
+    """Streaming log-radial: the window at global frame distance, cut at later chunks."""
+    from oracle.masks import frame_stride_for
+    mask = MaskSpec("log_radial_causal", chunk_frames=2, tile=2, radial_w0=4, radial_decay_log2=1,
+                    long_range_period=0)
+    for line in _read_golden("stream_radial_plan.txt"):
+        cap, cf, appends, query, tiles = (p.strip() for p in line.split(";"))
+        assert int(cf) == mask.chunk_frames
+        ring = oracle.RingCache(int(cap), 2, 3, 1, 2)
+        for a in appends.split():
+            t0, f = (int(x) for x in a.split(":"))
+            ring.append(None, None, f, t0, (2, 0, 0), 1e4)
+        phys, kt, ks = ring.key_layout(frame_stride_for(6))
+        qt0, qf = (int(x) for x in query.split(":"))
+        pos = oracle.token_positions(qf, 2, 3, qt0)
+        q_s = np.arange(qf * 6) % 6
+        qtiles = query_tiles(mask, qf, 6, qt0)
+        spans = plan_from_mask(mask, pos[:, 0], q_s, qtiles, phys, kt, ks)
+        want = [t.strip() for t in tiles.split("|")]
+        assert len(qtiles) == len(want)
+        for (q0, ql), sp, wt in zip(qtiles, spans, want):
+            head, body = wt.split(":")
+            assert [q0, ql] == [int(x) for x in head.split()]
+            assert sp == [tuple(int(x) for x in s.split()) for s in body.split(",")]
+
+
+def test_stream_radial_reductions():
+    """One chunk holding every frame gives the plain log-radial rule; a window covering every
+    piece with no long-range term gives the chunk-causal rule."""
+    rng = np.random.default_rng(5)
+    tq, tk = rng.integers(0, 40, (200, 1)), rng.integers(0, 40, (1, 200))
+    sq, sk = rng.integers(0, 1560, (200, 1)), rng.integers(0, 1560, (1, 200))
+    lr = MaskSpec("log_radial", tile=128, radial_w0=13, radial_decay_log2=1, long_range_period=8)
+    big = MaskSpec("log_radial_causal", chunk_frames=1000, tile=128, radial_w0=13, radial_decay_log2=1,
+                   long_range_period=8)
+    assert np.array_equal(allowed_mask(big, tq, sq, tk, sk), allowed_mask(lr, tq, sq, tk, sk))
+    wide = MaskSpec("log_radial_causal", chunk_frames=3, tile=128, radial_w0=1 << 20, radial_decay_log2=0,
+                    long_range_period=0)
+    cc = MaskSpec("chunk_causal", chunk_frames=3)
+    assert np.array_equal(allowed_mask(wide, tq, sq, tk, sk), allowed_mask(cc, tq, sq, tk, sk))
+    assert query_tiles(big, 2, 1560, 7) == query_tiles(lr, 2, 1560, 7)

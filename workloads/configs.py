@@ -27,8 +27,8 @@ from dataclasses import dataclass, field
 class MaskSpec:
     """Attention visibility rule.
 
-    kind: "dense" | "chunk_causal" | "log_radial".
-    chunk_frames: frames per causal chunk (chunk_causal).
+    kind: "dense" | "chunk_causal" | "log_radial" | "log_radial_causal".
+    chunk_frames: frames per causal chunk (chunk_causal, log_radial_causal).
     tile: query/key tile length in tokens used by the block plan.
     radial_w0, radial_decay_log2, long_range_period: log-radial window
       W(d) = ceil(w0 * 2**(-decay_log2 * d)) tiles at frame distance d; frames at a
@@ -180,6 +180,27 @@ _add(Workload(
     heads=2, head_dim=128, frame_h=30, frame_w=52, q_frames=3, q_t0=6, rope_dims=(44, 42, 42),
     theta=1e4, mask=MaskSpec("chunk_causal", chunk_frames=3), capacity=21,
     history=((0, 3), (3, 3)), data_scale=128 ** -0.5))
+
+_add(Workload(
+    name="stream_radial_chunk", seed=17,
+    description="Streaming log-radial, bf16: 12 heads, head_dim 128, 30x52 tokens per frame; query chunk of 3 "
+                "frames at t0=396 against a ring of the last 21 frames (378..398); log-radial window w0=13, decay "
+                "1/2, every 8th frame distance whole, restricted to block-causal 3-frame chunks; spatial "
+                "component 0.5.",
+    heads=12, head_dim=128, frame_h=30, frame_w=52, q_frames=3, q_t0=396, rope_dims=(44, 42, 42),
+    theta=1e4, mask=MaskSpec("log_radial_causal", chunk_frames=3, tile=128, radial_w0=13, radial_decay_log2=1,
+                             long_range_period=8),
+    capacity=21, history=_chunks(378, 396), lowfreq_amp=0.5))
+
+_add(Workload(
+    name="small_stream_radial", seed=18,
+    description="Streaming log-radial on a wrapped ring of 7 frames of 16x20 tokens (3 tiles per frame); the call "
+                "covers frames 13..15, which straddle 3-frame chunks 4 and 5, so frames 13 and 14 must not see "
+                "frame 15; w0=3, decay 1/2, period 4, 2 heads, head_dim 128, spatial component 0.5.",
+    heads=2, head_dim=128, frame_h=16, frame_w=20, q_frames=3, q_t0=13, rope_dims=(44, 42, 42),
+    theta=1e4, mask=MaskSpec("log_radial_causal", chunk_frames=3, tile=128, radial_w0=3, radial_decay_log2=1,
+                             long_range_period=4),
+    capacity=7, history=_chunks(4, 13), lowfreq_amp=0.5))
 
 WORKLOADS = dict(_W)
 
