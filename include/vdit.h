@@ -51,6 +51,7 @@ extern "C" {
 #define VDIT_MASK_DENSE 0
 #define VDIT_MASK_CHUNK_CAUSAL 1
 #define VDIT_MASK_LOG_RADIAL 2
+#define VDIT_MASK_LOG_RADIAL_CAUSAL 3
 /* OR-ed into the kind of the mask given to vdit_block_attn_fwd when its plan comes from
  * vdit_plan_dynamic (also set in such a plan's header kind word) */
 #define VDIT_MASK_FLAG_DYNAMIC 0x100
@@ -111,7 +112,12 @@ typedef struct {
  *   floor(tk / chunk_frames) <= floor(tq / chunk_frames).
  * LOG_RADIAL: with d = |tq - tk| and spatial tile indices (within-frame index / tile),
  *   a key is visible iff d == 0, or long_range_period > 0 and d % long_range_period == 0,
- *   or |tile_q - tile_k| <= W(d) = ceil(radial_w0 * 2^(-radial_decay_log2 * d)). */
+ *   or |tile_q - tile_k| <= W(d) = ceil(radial_w0 * 2^(-radial_decay_log2 * d))
+ *   ("DynamicRad ...", section 2, log-radial window; the full clip, symmetric in time).
+ * LOG_RADIAL_CAUSAL: streaming log-radial, the LOG_RADIAL rule at the global frame distance
+ *   and, in addition, floor(tk / chunk_frames) <= floor(tq / chunk_frames) (block-causal
+ *   chunks of the Wave Forcing page against the ring cache).  Query tiles are per frame, as
+ *   for LOG_RADIAL. */
 typedef struct {
     int32_t kind;
     int32_t chunk_frames;

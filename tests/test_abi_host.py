@@ -75,8 +75,8 @@ def test_host_plan_random_small_grids():
     """Random rules, grids, start frames and partly filled / wrapped rings."""
     from workloads.configs import MaskSpec, Workload
     rng = np.random.default_rng(123)
-    for trial in range(40):
-        kind = ["dense", "chunk_causal", "log_radial"][trial % 3]
+    for trial in range(48):
+        kind = ["dense", "chunk_causal", "log_radial", "log_radial_causal"][trial % 4]
         fh, fw = int(rng.integers(1, 14)), int(rng.integers(1, 30))
         cap = int(rng.integers(1, 9))
         frames = int(rng.integers(1, cap + 1))

@@ -30,7 +30,7 @@ from harness import compare, device_plan_words, run_workload
 pytestmark = pytest.mark.gpu
 
 CASES = [("small_chunk_pad", 0.0), ("small_chunk_pad", 0.4), ("small_radial", 0.3), ("small_radial", 1.0),
-         ("small_dense_d64", 0.5), ("wan13b_chunk_h2", 0.6), ("tiny", 0.5)]
+         ("small_dense_d64", 0.5), ("wan13b_chunk_h2", 0.6), ("tiny", 0.5), ("small_stream_radial", 0.4)]
 
 
 @pytest.fixture(scope="module", autouse=True)

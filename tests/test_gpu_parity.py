@@ -17,8 +17,9 @@ from harness import compare, device_plan_words, run_workload, sample_rows, sessi
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny", "tiny_d128", "small_chunk_pad", "small_radial", "small_dense_d64", "wan13b_chunk_h2"]
-LARGE = ["wan13b_chunk", "stream_wrap_straddle", "log_radial", "dense_clip", "stream14b_chunk"]
+SMALL = ["tiny", "tiny_d128", "small_chunk_pad", "small_radial", "small_dense_d64", "wan13b_chunk_h2",
+         "small_stream_radial"]
+LARGE = ["wan13b_chunk", "stream_wrap_straddle", "log_radial", "dense_clip", "stream14b_chunk", "stream_radial_chunk"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -144,7 +145,7 @@ def test_attention_parity_sampled(name):
         np.testing.assert_allclose(lse[h, rows], ref[h][1], atol=1e-2, rtol=0)
 
 
-@pytest.mark.parametrize("name", ["small_radial", "small_chunk_pad", "stream_wrap_straddle"])
+@pytest.mark.parametrize("name", ["small_radial", "small_chunk_pad", "stream_wrap_straddle", "small_stream_radial"])
 def test_zero_queries_average_visible_values(name):
     """Q = 0: every visible key gets the same weight, so O = mean of the visible V rows."""
     w = get_workload(name)

@@ -288,7 +288,7 @@ def test_log_radial_tile_pair_count_brute_force():
 
 
 @pytest.mark.parametrize("name", ["tiny", "small_chunk_pad", "small_radial", "small_dense_d64",
-                                  "stream_wrap_straddle"])
+                                  "stream_wrap_straddle", "small_stream_radial"])
 def test_plan_expands_to_element_mask(name):
     """Spans cover exactly the visible keys of every row of every query tile."""
     w = get_workload(name)

@@ -15,11 +15,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvdit.so"
 
 VDIT_OK, VDIT_ERR_INVALID_ARG, VDIT_ERR_BUFFER_TOO_SMALL, VDIT_ERR_UNSUPPORTED, VDIT_ERR_DEVICE = range(5)
 VDIT_DTYPE_BF16, VDIT_DTYPE_FP32 = 0, 1
-VDIT_MASK_DENSE, VDIT_MASK_CHUNK_CAUSAL, VDIT_MASK_LOG_RADIAL = 0, 1, 2
+VDIT_MASK_DENSE, VDIT_MASK_CHUNK_CAUSAL, VDIT_MASK_LOG_RADIAL, VDIT_MASK_LOG_RADIAL_CAUSAL = 0, 1, 2, 3
 VDIT_MASK_FLAG_DYNAMIC = 0x100
 VDIT_WHERE_HOST, VDIT_WHERE_DEVICE = 0, 1
 VDIT_PLAN_MAGIC = 0x54494456
-MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, "log_radial": VDIT_MASK_LOG_RADIAL}
+MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, "log_radial": VDIT_MASK_LOG_RADIAL,
+              "log_radial_causal": VDIT_MASK_LOG_RADIAL_CAUSAL}
 
 # every function declared in include/vdit.h
 EXPORTS = (

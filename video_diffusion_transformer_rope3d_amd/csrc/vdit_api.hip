@@ -121,12 +121,12 @@ int check_cache(const vdit_kv_cache* c) {
 
 int check_mask(const vdit_mask_cfg* m) {
     if (!m) return fail(VDIT_ERR_INVALID_ARG, "mask cfg is NULL");
-    if (m->kind != VDIT_MASK_DENSE && m->kind != VDIT_MASK_CHUNK_CAUSAL && m->kind != VDIT_MASK_LOG_RADIAL)
+    if (m->kind != VDIT_MASK_DENSE && m->kind != VDIT_MASK_CHUNK_CAUSAL && !is_radial(m->kind))
         return fail(VDIT_ERR_INVALID_ARG, "mask kind %d", m->kind);
     if (m->tile != 128) return fail(VDIT_ERR_UNSUPPORTED, "mask tile %d (supported: 128)", m->tile);
-    if (m->kind == VDIT_MASK_CHUNK_CAUSAL && m->chunk_frames < 1)
+    if ((m->kind == VDIT_MASK_CHUNK_CAUSAL || m->kind == VDIT_MASK_LOG_RADIAL_CAUSAL) && m->chunk_frames < 1)
         return fail(VDIT_ERR_INVALID_ARG, "chunk_frames %d must be >= 1", m->chunk_frames);
-    if (m->kind == VDIT_MASK_LOG_RADIAL &&
+    if (is_radial(m->kind) &&
         (m->radial_w0 < 0 || m->radial_decay_log2 < 0 || m->long_range_period < 0))
         return fail(VDIT_ERR_INVALID_ARG, "log-radial parameters must be >= 0");
     return VDIT_OK;
@@ -135,7 +135,8 @@ int check_mask(const vdit_mask_cfg* m) {
 PlanGeom make_geom(const vdit_mask_cfg* m, const vdit_grid& g, int32_t t0, const vdit_kv_cache* c) {
     PlanGeom pg;
     pg.kind = m->kind;
-    pg.chunk_frames = m->kind == VDIT_MASK_CHUNK_CAUSAL ? m->chunk_frames : 1;
+    pg.chunk_frames =
+        m->kind == VDIT_MASK_CHUNK_CAUSAL || m->kind == VDIT_MASK_LOG_RADIAL_CAUSAL ? m->chunk_frames : 1;
     pg.tile = m->tile;
     pg.w0 = m->radial_w0;
     pg.decay_log2 = m->radial_decay_log2;

@@ -957,7 +957,7 @@ template <int D, bool QF, bool OF>
 hipError_t launch_k(const AttnLaunch& L, const AttnArgs& a, hipStream_t s) {
     // neighbouring log-radial tiles (and tiles of dynamic plans) do not share span lists:
     // one tile per workgroup
-    if (L.mask_kind == VDIT_MASK_LOG_RADIAL || L.unpaired) return launch_tile<D, QF, OF>(a, s);
+    if (is_radial(L.mask_kind) || L.unpaired) return launch_tile<D, QF, OF>(a, s);
     return launch_unit<D, QF, OF>(a, L.n_qtiles * L.heads, s);
 }
 

@@ -37,11 +37,16 @@ __host__ __device__ inline int32_t radial_window(int32_t d, int32_t w0, int32_t 
     return (int32_t)(((int64_t)w0 + den - 1) >> sh);
 }
 
+// The log-radial rules (full clip and streaming): query tiles per frame, windowed key ranges.
+__host__ __device__ inline bool is_radial(int32_t kind) {
+    return kind == VDIT_MASK_LOG_RADIAL || kind == VDIT_MASK_LOG_RADIAL_CAUSAL;
+}
+
 // Number of mask units of the call and [first, end) call frames of unit u.
 __host__ __device__ inline int32_t plan_units(const PlanGeom& g) {
     if (g.frames <= 0) return 0;
     if (g.kind == VDIT_MASK_DENSE) return 1;
-    if (g.kind == VDIT_MASK_LOG_RADIAL) return g.frames;
+    if (is_radial(g.kind)) return g.frames;
     int32_t c0 = g.t0 / g.chunk_frames, c1 = (g.t0 + g.frames - 1) / g.chunk_frames;
     return c1 - c0 + 1;
 }
@@ -50,7 +55,7 @@ __host__ __device__ inline void plan_unit_frames(const PlanGeom& g, int32_t u, i
     if (g.kind == VDIT_MASK_DENSE) {
         *f_begin = 0;
         *f_end = g.frames;
-    } else if (g.kind == VDIT_MASK_LOG_RADIAL) {
+    } else if (is_radial(g.kind)) {
         *f_begin = u;
         *f_end = u + 1;
     } else {
@@ -111,11 +116,13 @@ __host__ __device__ inline bool plan_slot_range(const PlanGeom& g, const QTile& 
         *b = g.hw;
         return true;
     }
-    if (g.kind == VDIT_MASK_CHUNK_CAUSAL) {
+    if (g.kind == VDIT_MASK_CHUNK_CAUSAL || g.kind == VDIT_MASK_LOG_RADIAL_CAUSAL) {
         if (t / g.chunk_frames > qt.t_q / g.chunk_frames) return false;
-        *a = 0;
-        *b = g.hw;
-        return true;
+        if (g.kind == VDIT_MASK_CHUNK_CAUSAL) {
+            *a = 0;
+            *b = g.hw;
+            return true;
+        }
     }
     int32_t d = t > qt.t_q ? t - qt.t_q : qt.t_q - t;
     if (d == 0 || (g.period > 0 && d % g.period == 0)) {
