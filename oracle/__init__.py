@@ -20,7 +20,9 @@ numpy, written for a reader to check against the pages by eye:
 * attention - masked softmax attention (the exact result the method reaches);
 * dynamic   - the dynamic-threshold block plan (DynamicRad page, section 2, dual-mode
               strategy, mode 2): pooled pre-softmax logits of (query tile, key tile)
-              pairs as importance proxies and an adaptive threshold.
+              pairs as importance proxies and an adaptive threshold;
+* bwcache   - the block-wise feature reuse indicator (mean relative L1 distance of block
+              features between timesteps) and the reuse policy (BWCache page, section 2).
 
 Pins (see tests/test_oracle_*.py): RoPE against the RoFormer rotary implementation in
 `transformers` and against invariants (norm, relative offset, per-axis

@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ("test_oracle_pins.py", "test_oracle_dynamic.py")
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_dynamic.py", "test_oracle_bwcache.py")
 
 # (file under oracle/, original text, mutated text, what the mistake is)
 MUTATIONS = [
@@ -68,6 +68,17 @@ MUTATIONS = [
     ("masks.py", "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) <= window)",
      "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) < window)", "window edge excluded"),
     ("masks.py", "keep |= (d_b % mask.long_range_period) == 0", "pass", "long-range frames dropped"),
+    # block-reuse indicator and policy
+    ("bwcache.py", "num = np.abs(cur - prev).sum(axis=1)", "num = np.abs(cur).sum(axis=1) - np.abs(prev).sum(axis=1)",
+     "difference of norms instead of the norm of the difference"),
+    ("bwcache.py", "den = np.abs(prev).sum(axis=1)", "den = np.abs(cur).sum(axis=1)", "normalised by the current features"),
+    ("bwcache.py", "and self.run[b] + 1 < self.R", "and self.run[b] < self.R", "one reuse too many per interval"),
+    ("bwcache.py", "step >= self.total - self.first_reuse // 2", "step >= self.total - self.first_reuse",
+     "protected tail of k steps instead of k / 2"),
+    ("bwcache.py", "can = step > 0 and mean_rel_l1 < self.delta", "can = mean_rel_l1 < self.delta",
+     "reuse at the first step"),
+    ("bwcache.py", "can = False  # activating here", "pass  # activating here",
+     "activation inside its own protected tail"),
     ("masks.py", "        return radial & causal", "        return radial",
      "streaming log-radial sees later chunks"),
     ("masks.py", "        return radial & causal", "        return radial & causal & (np.asarray(tk) <= np.asarray(tq))",
