@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until reached)")
+    ap.add_argument("--rel-l1", action="store_true",
+                    help="time the block-reuse indicator (relative L1 of 30 blocks of 4680 x 1536 bf16 features)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one device-to-device copy of MIB MiB before timing (HBM counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -137,8 +139,66 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
     print(json.dumps(out))
 
 
+def bench_rel_l1(args):
+    """The block-wise reuse indicator on Wan-1.3B-shaped block features (30 blocks, one 3-frame
+    chunk of 4680 tokens x 1536 channels each, bf16): HBM-bound, 2 feature sets read once."""
+    import numpy as np
+    import torch
+
+    from video_diffusion_transformer_rope3d_amd import binding as B
+
+    nb, tokens, hidden = 30, 4680, 1536
+    elems = tokens * hidden
+    g = torch.Generator(device="cuda").manual_seed(0)
+    prev = torch.randn((nb, elems), device="cuda", generator=g).to(torch.bfloat16)
+    cur = (prev.float() + 0.05 * torch.randn((nb, elems), device="cuda", generator=g)).to(torch.bfloat16)
+    out = torch.empty(nb + 1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.vdit_block_rel_l1(cur, prev, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        B.vdit_block_rel_l1(cur, prev, out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    nbytes = 2 * nb * elems * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import bwcache
+        c0, p0 = cur[:1].float().cpu().numpy(), prev[:1].float().cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            bwcache.rel_l1(c0, p0)
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        cpu = {"value": round(elems * 2 * 2 / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"one block ({tokens} x {hidden} elements, bf16 values in fp64), {reps} passes"}
+    result = {
+        "metric": "block reuse indicator: feature bytes read per second", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan13b_block_features", "blocks": nb, "tokens": tokens, "hidden": hidden},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None},
+        "mean_rel_l1": float(out[-1].item()),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.rel_l1:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_rel_l1(args)
+        return
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.traffic_copy_mib, args.traffic_command)
         return

@@ -270,6 +270,47 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
                         const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
                         float softmax_scale, vdit_tensor o, float* lse, void* stream);
 
+/* ---- block-wise feature reuse ("BWCache: Accelerating Video Diffusion Transformers through
+ * Block-Wise Caching", section 2): the dynamic similarity indicator and the reuse decision.
+ *
+ * vdit_block_rel_l1: for every block b < n_blocks, the relative L1 distance
+ *   r_b = sum |cur_b - prev_b| / sum |prev_b| over the block's block_elems elements (0 when
+ *   both sums are 0, +inf when only the denominator is), and their mean.
+ * cur, prev: device, [n_blocks][block_stride] elements of `dtype` (VDIT_DTYPE_BF16 or _FP32),
+ *   the block's features first in each row; base pointers 16-byte aligned (NULL allowed when
+ *   block_elems == 0), block_stride >= block_elems and a multiple of 8 (bf16) or 4 (fp32).
+ * out_dev: device fp32 [n_blocks + 1]: r_0 .. r_{n_blocks-1}, then the mean.
+ * Arithmetic: fp32 sums over chunks of 32768 elements, chunk sums added in fp64 in chunk
+ *   order (deterministic).
+ * Memory: a workspace per (device, stream) for the chunk sums (8 bytes per chunk and block),
+ *   allocated (hipMalloc) on the first call that needs more and kept until the process ends.
+ * Errors: NULL pointers, n_blocks outside [1, 65535], block_elems < 0, bad stride or alignment
+ *   -> INVALID_ARG; other dtypes -> UNSUPPORTED. */
+int vdit_block_rel_l1(const void* cur, const void* prev, int32_t dtype, int32_t n_blocks, int64_t block_elems,
+                      int64_t block_stride, float* out_dev, void* stream);
+
+/* vdit_reuse_decide (host only): the reuse flags of every block at diffusion step `step`
+ * (0-based, < total_steps) given the latest indicator (the mean from vdit_block_rel_l1).
+ *   - The first step computes every block (nothing is cached).
+ *   - Otherwise every block reuses its cached features when mean_rel_l1 < delta, except a
+ *     block already reused reuse_interval - 1 times in a row, which is recomputed (periodic
+ *     recomputation; reuse_interval = 1 never reuses).
+ *   - When the first reuse happens at step k, the last floor(k / 2) steps recompute every
+ *     block; a first reuse that would fall inside its own protected tail does not happen.
+ * State (caller-owned, host): *first_reuse (-1 before any reuse) and run[n_blocks] (the
+ *   blocks' current runs of reuses, zero at the start); both are updated.
+ * reuse_out: host uint8 [n_blocks], 1 = reuse.
+ * Errors: NULL pointers, n_blocks < 1, reuse_interval < 1, step outside [0, total_steps) ->
+ *   INVALID_ARG. */
+typedef struct {
+    float delta;            /* reuse threshold on the mean relative L1 distance */
+    int32_t reuse_interval; /* R: at most R - 1 consecutive reuses of a block */
+    int32_t total_steps;    /* diffusion steps of the run */
+    int32_t n_blocks;
+} vdit_reuse_cfg;
+int vdit_reuse_decide(const vdit_reuse_cfg* cfg, int32_t step, float mean_rel_l1, int32_t* first_reuse, int32_t* run,
+                      uint8_t* reuse_out);
+
 #ifdef __cplusplus
 }
 #endif

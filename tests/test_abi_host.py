@@ -260,3 +260,51 @@ def test_dynamic_plan_errors(L):
     bad = B.dynamic_mask(B.mask_cfg(7))
     assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(bad), fake, 0.0, t, None,
                                  None) == B.VDIT_ERR_INVALID_ARG
+
+
+def test_reuse_policy_matches_oracle():
+    """vdit_reuse_decide (host) equals the oracle's policy on the golden schedules and on random
+    indicator sequences (values rounded to float32 first, as the ABI takes them)."""
+    import os
+    from oracle.bwcache import ReusePolicy
+    cases = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "bwcache_policy.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            nb, delta, r, total, ind, _ = (p.strip() for p in line.split(";"))
+            cases.append((int(nb), float(delta), int(r), int(total), [float(x) for x in ind.split()]))
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        total = int(rng.integers(1, 60))
+        cases.append((int(rng.integers(1, 5)), float(rng.uniform(0.01, 0.3)), int(rng.integers(1, 7)), total,
+                      rng.uniform(0.0, 0.4, total).tolist()))
+    for nb, delta, r, total, ind in cases:
+        delta32 = float(np.float32(delta))
+        ora = ReusePolicy(nb, delta32, r, total)
+        dev = B.ReuseState(nb, delta32, r, total)
+        for step, m in enumerate(ind):
+            m32 = float(np.float32(m))
+            assert dev.decide(step, m32) == ora.decide(step, m32), (nb, delta, r, total, step)
+        assert dev.first_reuse.value == ora.first_reuse
+
+
+def test_reuse_errors(L):
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    out = 0x20000
+    assert L.vdit_block_rel_l1(None, fake, B.VDIT_DTYPE_BF16, 2, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, 7, 2, 64, 64, out, None) == B.VDIT_ERR_UNSUPPORTED
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 0, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 70000, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 2, 64, 60, out, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 2, 60, 60, out, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake + 4, fake, B.VDIT_DTYPE_FP32, 2, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
+    cfg = B.VditReuseCfg(0.1, 0, 10, 2)
+    fr = ctypes.c_int32(-1)
+    run = (ctypes.c_int32 * 2)()
+    flags = (ctypes.c_uint8 * 2)()
+    assert L.vdit_reuse_decide(ctypes.byref(cfg), 0, ctypes.c_float(0.0), ctypes.byref(fr), run, flags) == \
+        B.VDIT_ERR_INVALID_ARG
+    cfg = B.VditReuseCfg(0.1, 3, 10, 2)
+    assert L.vdit_reuse_decide(ctypes.byref(cfg), 10, ctypes.c_float(0.0), ctypes.byref(fr), run, flags) == \
+        B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_reuse_decide(ctypes.byref(cfg), 0, ctypes.c_float(0.0), None, run, flags) == B.VDIT_ERR_INVALID_ARG

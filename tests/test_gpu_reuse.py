@@ -1,0 +1,92 @@
+"""GPU parity of the block-wise reuse indicator (vdit_block_rel_l1) against the oracle.
+
+Bar: every block's relative L1 and the mean within 1e-5 relative of the oracle's fp64 value
+(fp32 sums over 32768-element chunks, chunk sums combined in fp64: the fp32 error of one chunk
+is below 1e-6 relative for sums of non-negative terms); exact special cases (0, 1, 2, inf)
+where the definition gives them; repeated calls bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import bwcache
+from video_diffusion_transformer_rope3d_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def _features(shape, dtype, seed, drift=0.05):
+    g = torch.Generator().manual_seed(seed)
+    prev = torch.randn(shape, generator=g)
+    cur = prev + drift * torch.randn(shape, generator=g)
+    return cur.to(dtype), prev.to(dtype)
+
+
+def _check(cur, prev, got):
+    want = bwcache.rel_l1(cur.float().cpu().numpy(), prev.float().cpu().numpy())
+    got = got.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got[:-1], want, rtol=RTOL, atol=0)
+    np.testing.assert_allclose(got[-1], want.mean(), rtol=RTOL, atol=0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(3, 1000), (5, 70001), (2, 32768), (1, 7), (4, 65536 + 24)])
+def test_rel_l1_matches_oracle(dtype, shape):
+    print("rel_l1", dtype, shape, flush=True)
+    cur, prev = _features(shape, dtype, seed=shape[1])
+    align = 8 if dtype == torch.bfloat16 else 4
+    if shape[1] % align:  # rows padded to the stride multiple the ABI asks for
+        pad = (-shape[1]) % align
+        cur_p = torch.zeros((shape[0], shape[1] + pad), dtype=dtype)
+        prev_p = torch.zeros_like(cur_p)
+        cur_p[:, :shape[1]], prev_p[:, :shape[1]] = cur, prev
+        cd, pd = cur_p.cuda(), prev_p.cuda()
+        out = torch.empty(shape[0] + 1, dtype=torch.float32, device="cuda")
+        code = B.VDIT_DTYPE_BF16 if dtype == torch.bfloat16 else B.VDIT_DTYPE_FP32
+        B._check(B.lib().vdit_block_rel_l1(cd.data_ptr(), pd.data_ptr(), code, shape[0], shape[1],
+                                           cd.stride(0), out.data_ptr(), B._stream(None)))
+    else:
+        out = B.vdit_block_rel_l1(cur.cuda(), prev.cuda())
+    torch.cuda.synchronize()
+    _check(cur, prev, out)
+
+
+def test_rel_l1_special_cases():
+    x = torch.randn(6, 4096).cuda()
+    z = torch.zeros_like(x)
+    cur = torch.stack([x[0], -x[1], z[2], z[3], x[4], x[5]])
+    prev = torch.stack([x[0], x[1], x[2], z[3], z[4], x[5] * 2])
+    out = B.vdit_block_rel_l1(cur, prev).cpu().numpy()
+    assert out[0] == 0.0 and out[3] == 0.0 and np.isinf(out[4])
+    np.testing.assert_allclose(out[[1, 2, 5]], [2.0, 1.0, 0.5], rtol=1e-6)
+
+
+def test_rel_l1_empty_blocks_and_determinism():
+    e = torch.empty((3, 0), dtype=torch.bfloat16, device="cuda")
+    assert B.vdit_block_rel_l1(e, e).cpu().tolist() == [0.0, 0.0, 0.0, 0.0]
+    cur, prev = _features((7, 300000), torch.bfloat16, seed=4)
+    cur, prev = cur.cuda(), prev.cuda()
+    a, b = B.vdit_block_rel_l1(cur, prev), B.vdit_block_rel_l1(cur, prev)
+    assert torch.equal(a, b)
+
+
+def test_rel_l1_full_size_blocks():
+    """The benchmark's shape: 30 blocks of 4680 tokens x 1536 channels, bf16; every block
+    checked against the oracle one block at a time."""
+    nb, elems = 30, 4680 * 1536
+    g = torch.Generator(device="cuda").manual_seed(11)
+    prev = torch.randn((nb, elems), device="cuda", generator=g).to(torch.bfloat16)
+    cur = (prev.float() + 0.05 * torch.randn((nb, elems), device="cuda", generator=g)).to(torch.bfloat16)
+    out = B.vdit_block_rel_l1(cur, prev).cpu().numpy().astype(np.float64)
+    want = [bwcache.rel_l1(cur[b:b + 1].float().cpu().numpy(), prev[b:b + 1].float().cpu().numpy())[0]
+            for b in range(nb)]
+    np.testing.assert_allclose(out[:-1], want, rtol=RTOL, atol=0)
+    np.testing.assert_allclose(out[-1], np.mean(want), rtol=RTOL, atol=0)

@@ -27,8 +27,13 @@ EXPORTS = (
     "vdit_abi_version", "vdit_last_error", "vdit_status_string", "vdit_token_positions",
     "vdit_rope_table_build", "vdit_rope3d_qk", "vdit_kv_cache_bytes", "vdit_kv_cache_reset",
     "vdit_kv_append", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
-    "vdit_plan_dynamic", "vdit_block_attn_fwd",
+    "vdit_plan_dynamic", "vdit_block_attn_fwd", "vdit_block_rel_l1", "vdit_reuse_decide",
 )
+
+
+class VditReuseCfg(ctypes.Structure):
+    _fields_ = [("delta", ctypes.c_float), ("reuse_interval", ctypes.c_int32), ("total_steps", ctypes.c_int32),
+                ("n_blocks", ctypes.c_int32)]
 
 
 class VditTensor(ctypes.Structure):
@@ -105,6 +110,9 @@ def lib():
             "vdit_block_attn_fwd": (I32, [VditTensor, ctypes.POINTER(VditRopeCfg), VditGrid, I32,
                                           ctypes.POINTER(VditKVCache), ctypes.POINTER(VditMaskCfg), P,
                                           ctypes.c_float, VditTensor, P, P]),
+            "vdit_block_rel_l1": (I32, [P, P, I32, I32, ctypes.c_int64, ctypes.c_int64, P, P]),
+            "vdit_reuse_decide": (I32, [ctypes.POINTER(VditReuseCfg), I32, ctypes.c_float, ctypes.POINTER(I32),
+                                        P, P]),
         }
         for name in EXPORTS:
             fn = getattr(L, name)
@@ -322,3 +330,40 @@ def plan_fields(plan):
     rp = p[8 + 2 * nq:8 + 3 * nq + 1]
     sp = p[8 + 3 * nq + 1:8 + 3 * nq + 1 + 2 * ns].reshape(ns, 2)
     return p[:8], qt, rp, sp
+
+
+def vdit_block_rel_l1(cur, prev, out=None, stream=None):
+    """Relative L1 distance of every block between two feature sets ([blocks][...] device
+    tensors, bf16 or fp32, rows contiguous) and their mean: fp32 tensor [blocks + 1]."""
+    import torch
+    if cur.shape != prev.shape or cur.dtype != prev.dtype:
+        raise ValueError("cur and prev must have one shape and dtype")
+    nb = cur.shape[0]
+    cur2, prev2 = cur.reshape(nb, -1), prev.reshape(nb, -1)
+    if cur2.stride(1) != 1 or prev2.stride(1) != 1 or cur2.stride(0) != prev2.stride(0):
+        raise ValueError("blocks must be rows with contiguous elements and one stride")
+    dt = {torch.bfloat16: VDIT_DTYPE_BF16, torch.float32: VDIT_DTYPE_FP32}.get(cur.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {cur.dtype}")
+    out = torch.empty(nb + 1, dtype=torch.float32, device=cur.device) if out is None else out
+    stride = cur2.stride(0) if cur2.shape[1] > 0 else 0  # empty blocks: nothing is read
+    _check(lib().vdit_block_rel_l1(cur2.data_ptr(), prev2.data_ptr(), dt, nb, cur2.shape[1], stride,
+                                   out.data_ptr(), _stream(stream)))
+    return out
+
+
+class ReuseState:
+    """Caller-side state of vdit_reuse_decide: the first reuse step and per-block runs."""
+
+    def __init__(self, n_blocks: int, delta: float, reuse_interval: int, total_steps: int):
+        self.cfg = VditReuseCfg(delta, reuse_interval, total_steps, n_blocks)
+        self.first_reuse = ctypes.c_int32(-1)
+        self.run = (ctypes.c_int32 * n_blocks)()
+        self._out = (ctypes.c_uint8 * n_blocks)()
+
+    def decide(self, step: int, mean_rel_l1: float):
+        _check(lib().vdit_reuse_decide(ctypes.byref(self.cfg), step, ctypes.c_float(mean_rel_l1),
+                                       ctypes.byref(self.first_reuse), ctypes.addressof(self.run),
+                                       ctypes.addressof(self._out)))
+        return [bool(x) for x in self._out]
+

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvdit.so")
-SOURCES = ["vdit_api.hip", "vdit_kernels.hip", "vdit_attn.hip", "vdit_dynamic.hip"]
+SOURCES = ["vdit_api.hip", "vdit_kernels.hip", "vdit_attn.hip", "vdit_dynamic.hip", "vdit_reuse.hip"]
 
 
 def hipcc() -> str:

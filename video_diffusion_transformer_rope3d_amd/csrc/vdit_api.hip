@@ -490,4 +490,48 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
     return device_status(launch_attn_fwd(a, (hipStream_t)stream), "attention kernel");
 }
 
+int vdit_block_rel_l1(const void* cur, const void* prev, int32_t dtype, int32_t n_blocks, int64_t block_elems,
+                      int64_t block_stride, float* out_dev, void* stream) {
+    if (!out_dev) return fail(VDIT_ERR_INVALID_ARG, "out is NULL");
+    if (block_elems > 0 && (!cur || !prev)) return fail(VDIT_ERR_INVALID_ARG, "cur and prev must be set");
+    if (dtype != VDIT_DTYPE_BF16 && dtype != VDIT_DTYPE_FP32)
+        return fail(VDIT_ERR_UNSUPPORTED, "dtype %d is not bf16 or fp32", dtype);
+    if (n_blocks < 1 || n_blocks > 65535) return fail(VDIT_ERR_INVALID_ARG, "n_blocks %d outside [1, 65535]", n_blocks);
+    if (block_elems < 0 || block_stride < block_elems)
+        return fail(VDIT_ERR_INVALID_ARG, "block_elems %lld, block_stride %lld", (long long)block_elems,
+                    (long long)block_stride);
+    const int64_t align = dtype == VDIT_DTYPE_BF16 ? 8 : 4;
+    if (block_stride % align) return fail(VDIT_ERR_INVALID_ARG, "block_stride must be a multiple of %lld", (long long)align);
+    if (((uintptr_t)cur & 15) || ((uintptr_t)prev & 15))
+        return fail(VDIT_ERR_INVALID_ARG, "feature pointers must be 16-byte aligned");
+    if (((uintptr_t)out_dev & 3)) return fail(VDIT_ERR_INVALID_ARG, "out not 4-byte aligned");
+    return device_status(launch_rel_l1(cur, prev, dtype == VDIT_DTYPE_FP32, n_blocks, block_elems, block_stride,
+                                       out_dev, (hipStream_t)stream),
+                         "relative L1 kernels");
+}
+
+int vdit_reuse_decide(const vdit_reuse_cfg* cfg, int32_t step, float mean_rel_l1, int32_t* first_reuse, int32_t* run,
+                      uint8_t* reuse_out) {
+    if (!cfg || !first_reuse || !run || !reuse_out) return fail(VDIT_ERR_INVALID_ARG, "NULL argument");
+    if (cfg->n_blocks < 1 || cfg->reuse_interval < 1 || cfg->total_steps < 1)
+        return fail(VDIT_ERR_INVALID_ARG, "n_blocks %d, reuse_interval %d, total_steps %d must be >= 1",
+                    cfg->n_blocks, cfg->reuse_interval, cfg->total_steps);
+    if (step < 0 || step >= cfg->total_steps)
+        return fail(VDIT_ERR_INVALID_ARG, "step %d outside [0, %d)", step, cfg->total_steps);
+    const int32_t k = *first_reuse;
+    const bool protected_tail = k >= 0 && step >= cfg->total_steps - k / 2;
+    bool can = step > 0 && mean_rel_l1 < cfg->delta && !protected_tail;
+    // a first reuse here would put this very step inside its own protected tail
+    if (can && k < 0 && step >= cfg->total_steps - step / 2) can = false;
+    bool any = false;
+    for (int32_t b = 0; b < cfg->n_blocks; ++b) {
+        const bool r = can && run[b] + 1 < cfg->reuse_interval;
+        reuse_out[b] = r ? 1 : 0;
+        any = any || r;
+    }
+    if (any && k < 0) *first_reuse = step;
+    for (int32_t b = 0; b < cfg->n_blocks; ++b) run[b] = reuse_out[b] ? run[b] + 1 : 0;
+    return ok();
+}
+
 }  // extern "C"

@@ -213,6 +213,8 @@ struct DynLaunch {
     int32_t* plan;
 };
 hipError_t launch_plan_dynamic(const DynLaunch& a, hipStream_t s);
+hipError_t launch_rel_l1(const void* cur, const void* prev, bool f32, int32_t n_blocks, int64_t block_elems,
+                         int64_t block_stride, float* out, hipStream_t s);
 
 // Query tiles one attention call can hold (its unit table lives in LDS).
 constexpr int32_t kAttnMaxQTiles = 4096;
