@@ -21,6 +21,8 @@ numpy, written for a reader to check against the pages by eye:
 * dynamic   - the dynamic-threshold block plan (DynamicRad page, section 2, dual-mode
               strategy, mode 2): pooled pre-softmax logits of (query tile, key tile)
               pairs as importance proxies and an adaptive threshold;
+* projection- the fused QKV projection with RoPE at the global time index and the K/V
+              append (Causal-RoPE SP page, section 2.C, fused QKV + RoPE);
 * bwcache   - the block-wise feature reuse indicator (mean relative L1 distance of block
               features between timesteps) and the reuse policy (BWCache page, section 2).
 

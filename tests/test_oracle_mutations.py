@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ("test_oracle_pins.py", "test_oracle_dynamic.py", "test_oracle_bwcache.py")
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_dynamic.py", "test_oracle_bwcache.py", "test_oracle_projection.py")
 
 # (file under oracle/, original text, mutated text, what the mistake is)
 MUTATIONS = [
@@ -68,6 +68,17 @@ MUTATIONS = [
     ("masks.py", "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) <= window)",
      "keep = (d_b == 0) | (np.broadcast_to(tile_gap, shape) < window)", "window edge excluded"),
     ("masks.py", "keep |= (d_b % mask.long_range_period) == 0", "pass", "long-range frames dropped"),
+    # fused QKV projection
+    ("projection.py", "    y = x @ w.T\n", "    y = (x @ w.T)[:, ::-1]\n",
+     "output features reversed"),
+    ("projection.py", "        y = y + np.asarray(b, dtype=np.float64)[None, :]", "        pass", "bias dropped"),
+    ("projection.py", "q, k, v = y[:, :hd], y[:, hd:2 * hd], y[:, 2 * hd:3 * hd]",
+     "k, q, v = y[:, :hd], y[:, hd:2 * hd], y[:, 2 * hd:3 * hd]", "Q and K rows swapped"),
+    ("projection.py", "return (q.reshape(-1, heads, head_dim), k.reshape(-1, heads, head_dim), v.reshape(-1, heads, head_dim))",
+     "return (q.reshape(-1, head_dim, heads).transpose(0, 2, 1), k.reshape(-1, heads, head_dim), v.reshape(-1, heads, head_dim))",
+     "Q rows channel-major instead of head-major"),
+    ("projection.py", "    pos = token_positions(frames, ring.frame_h, ring.frame_w, t0)",
+     "    pos = token_positions(frames, ring.frame_h, ring.frame_w, 0)", "Q rotated at local positions"),
     # block-reuse indicator and policy
     ("bwcache.py", "num = np.abs(cur - prev).sum(axis=1)", "num = np.abs(cur).sum(axis=1) - np.abs(prev).sum(axis=1)",
      "difference of norms instead of the norm of the difference"),
