@@ -270,6 +270,29 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
                         const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
                         float softmax_scale, vdit_tensor o, float* lse, void* stream);
 
+/* ---- fused QKV projection + RoPE3D + K/V append ("Accelerating Video Generation Inference ...",
+ * section 2.C, the QKV projection and the rotary embedding as one kernel with precomputed
+ * tables; section 2.B, global positions; section 2.A, the KV cache).
+ * qkv = x W^T + b for the call's frames*height*width tokens; the Q part is rotated at
+ * (t0 + f, h, w) and written to q_out; the K part is rotated and the V part copied into the
+ * ring slots t mod capacity, exactly as vdit_kv_append would store them (slot tables and the
+ * zeroed pad tokens included).  One rounding to bf16 after the fp32 accumulation, bias and
+ * rotation.
+ * x: device bf16, row n = token n of the call (frame-major, then h, w), hidden elements per
+ *   row, rows stride_token elements apart (a multiple of 8); stride_head and reserved unused / 0.
+ * w_qkv: device bf16 [3 * heads * head_dim][w_stride] (row pitch w_stride >= hidden, a multiple
+ *   of 8): rows 0 .. HD-1 give Q, HD .. 2HD-1 K, 2HD .. 3HD-1 V, each block head-major (row
+ *   h * head_dim + d), HD = heads * head_dim of the cache.
+ * b_qkv: NULL or device fp32 [3 * heads * head_dim].
+ * q_out: bf16 [tokens][heads][head_dim] (device).  rope: as for vdit_kv_append (NULL: no
+ *   rotation).
+ * Errors: as vdit_kv_append; hidden not a positive multiple of 64, heads * head_dim not a
+ *   multiple of 128, x / q_out not bf16, x or W spanning 4 GiB or more -> UNSUPPORTED; bad
+ *   strides or alignment -> INVALID_ARG. */
+int vdit_qkv_rope_append(vdit_tensor x, int32_t hidden, const void* w_qkv, int64_t w_stride, const float* b_qkv,
+                         const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0, vdit_kv_cache* cache, vdit_tensor q_out,
+                         void* stream);
+
 /* ---- block-wise feature reuse ("BWCache: Accelerating Video Diffusion Transformers through
  * Block-Wise Caching", section 2): the dynamic similarity indicator and the reuse decision.
  *

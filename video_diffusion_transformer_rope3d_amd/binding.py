@@ -27,7 +27,7 @@ EXPORTS = (
     "vdit_abi_version", "vdit_last_error", "vdit_status_string", "vdit_token_positions",
     "vdit_rope_table_build", "vdit_rope3d_qk", "vdit_kv_cache_bytes", "vdit_kv_cache_reset",
     "vdit_kv_append", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
-    "vdit_plan_dynamic", "vdit_block_attn_fwd", "vdit_block_rel_l1", "vdit_reuse_decide",
+    "vdit_plan_dynamic", "vdit_block_attn_fwd", "vdit_block_rel_l1", "vdit_reuse_decide", "vdit_qkv_rope_append",
 )
 
 
@@ -110,6 +110,8 @@ def lib():
             "vdit_block_attn_fwd": (I32, [VditTensor, ctypes.POINTER(VditRopeCfg), VditGrid, I32,
                                           ctypes.POINTER(VditKVCache), ctypes.POINTER(VditMaskCfg), P,
                                           ctypes.c_float, VditTensor, P, P]),
+            "vdit_qkv_rope_append": (I32, [VditTensor, I32, P, ctypes.c_int64, P, ctypes.POINTER(VditRopeCfg),
+                                           VditGrid, I32, ctypes.POINTER(VditKVCache), VditTensor, P]),
             "vdit_block_rel_l1": (I32, [P, P, I32, I32, ctypes.c_int64, ctypes.c_int64, P, P]),
             "vdit_reuse_decide": (I32, [ctypes.POINTER(VditReuseCfg), I32, ctypes.c_float, ctypes.POINTER(I32),
                                         P, P]),
@@ -366,4 +368,21 @@ class ReuseState:
                                        ctypes.byref(self.first_reuse), ctypes.addressof(self.run),
                                        ctypes.addressof(self._out)))
         return [bool(x) for x in self._out]
+
+
+def vdit_qkv_rope_append(x, w_qkv, b_qkv, rope, g: VditGrid, t0: int, cache: "KVCache", q_out=None, stream=None):
+    """x [tokens][hidden] bf16, w_qkv [3 H D][hidden] bf16, b_qkv fp32 [3 H D] or None (device
+    tensors): Q rotated (returned, [tokens][H][D] bf16); K, V appended to `cache`."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1 or w_qkv.dim() != 2 or w_qkv.stride(1) != 1:
+        raise ValueError("x and w_qkv must be 2-D with contiguous rows")
+    d = cache.desc
+    q_out = torch.empty((x.shape[0], d.heads, d.head_dim), dtype=torch.bfloat16, device=x.device) \
+        if q_out is None else q_out
+    xt = VditTensor(x.data_ptr(), VDIT_DTYPE_BF16 if x.dtype == torch.bfloat16 else -1, 0, x.stride(0), 0)
+    rp = ctypes.byref(rope.cfg) if rope is not None else None
+    _check(lib().vdit_qkv_rope_append(xt, x.shape[1], w_qkv.data_ptr(), w_qkv.stride(0),
+                                      None if b_qkv is None else b_qkv.data_ptr(), rp, g, t0,
+                                      ctypes.byref(d), tensor(q_out), _stream(stream)))
+    return q_out
 

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvdit.so")
-SOURCES = ["vdit_api.hip", "vdit_kernels.hip", "vdit_attn.hip", "vdit_dynamic.hip", "vdit_reuse.hip"]
+SOURCES = ["vdit_api.hip", "vdit_kernels.hip", "vdit_attn.hip", "vdit_dynamic.hip", "vdit_reuse.hip",
+           "vdit_proj.hip"]
 
 
 def hipcc() -> str:

@@ -534,4 +534,69 @@ int vdit_reuse_decide(const vdit_reuse_cfg* cfg, int32_t step, float mean_rel_l1
     return ok();
 }
 
+int vdit_qkv_rope_append(vdit_tensor x, int32_t hidden, const void* w_qkv, int64_t w_stride, const float* b_qkv,
+                         const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0, vdit_kv_cache* c, vdit_tensor q_out,
+                         void* stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!c->k || !c->v || !c->slot_frame_dev || !c->slot_frame_host)
+        return fail(VDIT_ERR_INVALID_ARG, "cache buffers must be set");
+    if ((st = check_grid(grid))) return st;
+    if (grid.height * grid.width != c->tokens_per_frame)
+        return fail(VDIT_ERR_INVALID_ARG, "grid has %d tokens per frame, cache %d", grid.height * grid.width,
+                    c->tokens_per_frame);
+    if (grid.frames < 1 || grid.frames > c->capacity)
+        return fail(VDIT_ERR_INVALID_ARG, "frames %d must be in [1, capacity %d]", grid.frames, c->capacity);
+    if (t0 < 0 || (int64_t)t0 + grid.frames > INT32_MAX / 2) return fail(VDIT_ERR_INVALID_ARG, "t0 %d out of range", t0);
+    if (hidden < 64 || hidden % 64) return fail(VDIT_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 64", hidden);
+    if ((c->heads * c->head_dim) % 128)
+        return fail(VDIT_ERR_UNSUPPORTED, "heads x head_dim %d must be a multiple of 128", c->heads * c->head_dim);
+    if (!w_qkv || ((uintptr_t)w_qkv & 15)) return fail(VDIT_ERR_INVALID_ARG, "w_qkv NULL or not 16-byte aligned");
+    if (w_stride < hidden || w_stride % 8) return fail(VDIT_ERR_INVALID_ARG, "w_stride %lld", (long long)w_stride);
+    if (b_qkv && ((uintptr_t)b_qkv & 3)) return fail(VDIT_ERR_INVALID_ARG, "b_qkv not 4-byte aligned");
+    const int32_t n = grid.frames * c->tokens_per_frame;
+    if (!x.data || x.dtype != VDIT_DTYPE_BF16 || x.reserved)
+        return fail(x.data && x.dtype != VDIT_DTYPE_BF16 ? VDIT_ERR_UNSUPPORTED : VDIT_ERR_INVALID_ARG,
+                    "x must be bf16 device data");
+    if (((uintptr_t)x.data & 15) || x.stride_token < hidden || x.stride_token % 8)
+        return fail(VDIT_ERR_INVALID_ARG, "x: 16-byte aligned rows of at least hidden elements, stride a multiple of 8");
+    if ((st = check_tensor(q_out, "q_out", n, c->heads, c->head_dim))) return st;
+    if (q_out.dtype != VDIT_DTYPE_BF16) return fail(VDIT_ERR_UNSUPPORTED, "q_out must be bf16");
+    const int64_t w_bytes = ((int64_t)3 * c->heads * c->head_dim - 1) * w_stride * 2 + (int64_t)hidden * 2;
+    const int64_t x_bytes = ((int64_t)n - 1) * x.stride_token * 2 + (int64_t)hidden * 2;
+    if (w_bytes >= ((int64_t)1 << 32) || x_bytes >= ((int64_t)1 << 32))
+        return fail(VDIT_ERR_UNSUPPORTED, "x or w_qkv span 4 GiB or more");
+    ProjLaunch L{};
+    if (rope) {
+        if ((st = check_rope_use(rope, c->head_dim, grid, t0))) return st;
+        L.rope = rope_dev(rope);
+        L.has_rope = true;
+    }
+    L.x = x.data;
+    L.x_st = x.stride_token;
+    L.n_tokens = n;
+    L.hidden = hidden;
+    L.w = w_qkv;
+    L.w_st = w_stride;
+    L.bias = b_qkv;
+    L.heads = c->heads;
+    L.head_dim = c->head_dim;
+    L.hw = c->tokens_per_frame;
+    L.wf = grid.width;
+    L.t0 = t0;
+    L.q = q_out.data;
+    L.q_st = q_out.stride_token;
+    L.q_sh = q_out.stride_head;
+    L.kc = c->k;
+    L.vt = c->v;
+    L.frame_stride = frame_stride_of(c->tokens_per_frame);
+    L.kv_rows = (int64_t)c->capacity * L.frame_stride;
+    L.capacity = c->capacity;
+    hipError_t e = launch_qkv_rope_append(L, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_kv_finish(*c, grid, t0, (hipStream_t)stream);
+    if (e != hipSuccess) return device_status(e, "projection kernels");
+    for (int32_t f = 0; f < grid.frames; ++f) c->slot_frame_host[(t0 + f) % c->capacity] = t0 + f;
+    return ok();
+}
+
 }  // extern "C"

@@ -213,6 +213,29 @@ struct DynLaunch {
     int32_t* plan;
 };
 hipError_t launch_plan_dynamic(const DynLaunch& a, hipStream_t s);
+// Fused QKV projection + RoPE + K/V append (validated by the caller).
+struct ProjLaunch {
+    const void* x;
+    int64_t x_st;
+    int32_t n_tokens, hidden;
+    const void* w;
+    int64_t w_st;
+    const float* bias;
+    int32_t heads, head_dim;
+    RopeDev rope;
+    bool has_rope;
+    int32_t hw, wf, t0;
+    void* q;
+    int64_t q_st, q_sh;
+    void* kc;
+    void* vt;
+    int64_t kv_rows;
+    int32_t frame_stride, capacity;
+};
+hipError_t launch_qkv_rope_append(const ProjLaunch& L, hipStream_t s);
+// After K/V rows of frames t0 .. t0 + frames - 1 were written by another kernel: the device slot
+// table and the zero pad tokens of those slots, as the append does.
+hipError_t launch_kv_finish(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s);
 hipError_t launch_rel_l1(const void* cur, const void* prev, bool f32, int32_t n_blocks, int64_t block_elems,
                          int64_t block_stride, float* out, hipStream_t s);
 
