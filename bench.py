@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until reached)")
+    ap.add_argument("--qkv", action="store_true",
+                    help="time the fused QKV projection + RoPE + K/V append of the Wan-1.3B chunk")
     ap.add_argument("--rel-l1", action="store_true",
                     help="time the block-reuse indicator (relative L1 of 30 blocks of 4680 x 1536 bf16 features)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -191,8 +193,73 @@ def bench_rel_l1(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_qkv(args):
+    """The fused QKV projection of one Wan-1.3B-shaped chunk: x [4680 x 1536] bf16 times
+    W_qkv [4608 x 1536] bf16 (random, 1/sqrt(1536) scale) plus bias, Q rotated out, K and V
+    rotated / copied into a 21-frame ring (frames 6..8)."""
+    import numpy as np
+    import torch
+
+    from video_diffusion_transformer_rope3d_amd import binding as B
+
+    heads, d, hidden, fh, fw, frames, t0, cap = 12, 128, 1536, 30, 52, 3, 6, 21
+    n = frames * fh * fw
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((n, hidden), device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn((3 * heads * d, hidden), device="cuda", generator=g) / hidden ** 0.5).to(torch.bfloat16)
+    b = 0.1 * torch.randn(3 * heads * d, device="cuda", generator=g)
+    rope = B.Rope(d, (44, 42, 42), 1e4, t0 + frames + 4, fh, fw)
+    cache = B.KVCache(cap, fh * fw, heads, d)
+    q = torch.empty((n, heads, d), dtype=torch.bfloat16, device="cuda")
+    grid = B.grid(frames, fh, fw)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.vdit_qkv_rope_append(x, w, b, rope, grid, t0, cache, q_out=q)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        B.vdit_qkv_rope_append(x, w, b, rope, grid, t0, cache, q_out=q)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    flop = 2.0 * n * 3 * heads * d * hidden
+    tf = flop / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import projection
+        import oracle
+        rows = 64  # a bounded sample: 64 tokens through the oracle
+        xs, ws, bs = x[:rows].float().cpu().numpy(), w.float().cpu().numpy(), b.cpu().numpy()
+        t_start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t_start < min(args.cpu_seconds, 10.0):
+            ring = oracle.RingCache(cap, 1, rows, heads, d)
+            projection.qkv_rope_append(xs, ws, bs, ring, 1, t0, (44, 42, 42), 1e4)
+            reps += 1
+        sec = (time.perf_counter() - t_start) / reps
+        cpu = {"value": round(2.0 * rows * 3 * heads * d * hidden / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+               "kind": "oracle", "sample": f"{rows} tokens of the chunk (one 1 x {rows} frame), {reps} passes"}
+    result = {
+        "metric": "fused QKV projection + RoPE + KV append TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan13b_chunk_qkv", "tokens": n, "hidden": hidden, "heads": heads, "head_dim": d},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.qkv:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_qkv(args)
+        return
     if args.rel_l1:
         if args.gpus != 1:
             print("bench.py measures one GPU only", file=sys.stderr)

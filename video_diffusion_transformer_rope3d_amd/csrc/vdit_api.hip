@@ -592,8 +592,10 @@ int vdit_qkv_rope_append(vdit_tensor x, int32_t hidden, const void* w_qkv, int64
     L.frame_stride = frame_stride_of(c->tokens_per_frame);
     L.kv_rows = (int64_t)c->capacity * L.frame_stride;
     L.capacity = c->capacity;
+    L.slot_frame = c->slot_frame_dev;
+    L.frames = grid.frames;
     hipError_t e = launch_qkv_rope_append(L, (hipStream_t)stream);
-    if (e == hipSuccess) e = launch_kv_finish(*c, grid, t0, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_kv_zero_pad(*c, grid, t0, (hipStream_t)stream);
     if (e != hipSuccess) return device_status(e, "projection kernels");
     for (int32_t f = 0; f < grid.frames; ++f) c->slot_frame_host[(t0 + f) % c->capacity] = t0 + f;
     return ok();

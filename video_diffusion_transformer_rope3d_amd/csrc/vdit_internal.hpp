@@ -231,11 +231,13 @@ struct ProjLaunch {
     void* vt;
     int64_t kv_rows;
     int32_t frame_stride, capacity;
+    int32_t* slot_frame;  // device slot table (written by the kernel)
+    int32_t frames;
 };
 hipError_t launch_qkv_rope_append(const ProjLaunch& L, hipStream_t s);
-// After K/V rows of frames t0 .. t0 + frames - 1 were written by another kernel: the device slot
-// table and the zero pad tokens of those slots, as the append does.
-hipError_t launch_kv_finish(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s);
+// After K/V rows of frames t0 .. t0 + frames - 1 were written by another kernel: zeros in the pad
+// tokens of those slots (when frames are padded), as the append does.
+hipError_t launch_kv_zero_pad(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s);
 hipError_t launch_rel_l1(const void* cur, const void* prev, bool f32, int32_t n_blocks, int64_t block_elems,
                          int64_t block_stride, float* out, hipStream_t s);
 

@@ -274,14 +274,9 @@ hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid 
     return hipGetLastError();
 }
 
-__global__ void slot_write_kernel(int32_t t0, int32_t capacity, int32_t frames, int32_t* slot_frame) {
-    for (int32_t f = threadIdx.x; f < frames; f += blockDim.x) slot_frame[(t0 + f) % capacity] = t0 + f;
-}
-
-hipError_t launch_kv_finish(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s) {
+hipError_t launch_kv_zero_pad(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s) {
     const int32_t hw = c.tokens_per_frame, fs = frame_stride_of(hw);
     const int64_t kv_rows = (int64_t)c.capacity * fs;
-    slot_write_kernel<<<1, 256, 0, s>>>(t0, c.capacity, grid.frames, c.slot_frame_dev);
     if (fs > hw) {
         if (c.head_dim == 128)
             kv_zero_pad_kernel<128><<<dim3(grid.frames, c.heads), kThreads, 0, s>>>(
