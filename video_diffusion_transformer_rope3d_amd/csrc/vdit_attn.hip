@@ -314,7 +314,10 @@ __device__ __forceinline__ void tile_step(const char* kst, const FragLane& fl, c
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // the row's other half (lane ^ 32) through a lane swap on the VALU: an LDS permute would
+    // also wait for the V^T fragment reads issued above
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     if (__any(mt > m_run + lazy_raw)) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = fast_exp2((m_run - m_new) * c);
@@ -325,15 +328,21 @@ __device__ __forceinline__ void tile_step(const char* kst, const FragLane& fl, c
     }
     const float mc = -m_run * c;
     bf16x8 pk[4];
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(__builtin_fmaf(sacc[j >> 1][(j & 1) * 8 + e], c, mc));
-            l_run += p[e];
-        }
-        pk[j] = __builtin_bit_cast(bf16x8, pack_bf16x8(p));
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[j >> 1][(j & 1) * 8 + e], c, mc));
+        const u32x4 u = pack_bf16x8(p);
+        pk[j] = __builtin_bit_cast(bf16x8, u);
+        // the row sum adds the bf16-rounded P (the weights P.V uses), two per dot product;
+        // the words are named (a bit_cast of a vector subscript in an unrolled loop is
+        // compiled as reads of the first word only)
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), one2, l_run, false);
     }
     sched_fence();
     // O^T += V^T P^T
