@@ -13,10 +13,13 @@
  *   touched.  vdit_last_error() returns a message for the calling thread's last error.
  *   Faults inside a kernel surface at the caller's next synchronisation; a launch the
  *   runtime rejects returns VDIT_ERR_DEVICE.
- * - Memory: every buffer is allocated and owned by the caller.  Pointers documented
- *   "device" must be device memory of the current HIP device, "host" plain host memory.
- *   The library allocates no device memory and keeps no global state besides the
- *   per-thread error string.
+ * - Memory: every buffer passed in is allocated and owned by the caller.  Pointers
+ *   documented "device" must be device memory of the current HIP device, "host" plain
+ *   host memory.  Three calls keep a scratch workspace of their own per (device, stream),
+ *   allocated on first need and kept until the process ends, each documented at the call:
+ *   vdit_block_attn_fwd (split-unit partials and counters), vdit_plan_dynamic (pooled
+ *   tiles and proxies) and vdit_block_rel_l1 (per-chunk partial sums).  Besides those
+ *   and the per-thread error string the library keeps no global state.
  * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
  *   work is only enqueued; no call synchronises the device.
  * - Tensors [tokens][heads][channels]: vdit_tensor gives the base pointer, dtype and the
