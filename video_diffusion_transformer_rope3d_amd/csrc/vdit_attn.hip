@@ -59,6 +59,7 @@ struct AttnArgs {
     float scale_log2;
     int32_t* cnt;  // per-tile arrival counters, zero between calls
     float* part;   // partial results, two slots per workgroup
+    const int32_t* order;  // tile kernel: query tiles longest first (NULL: plan order)
 };
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -415,8 +416,15 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, g = lane >> 5;
-    const int item = xcd_remap(blockIdx.x, a.n_qtiles * a.heads);
-    const int h = item / a.n_qtiles, qt = item % a.n_qtiles;
+    int h, qt;
+    if (a.order) {  // longest tiles first, all heads of a tile together
+        qt = a.order[blockIdx.x / a.heads];
+        h = blockIdx.x % a.heads;
+    } else {
+        const int item = xcd_remap(blockIdx.x, a.n_qtiles * a.heads);
+        h = item / a.n_qtiles;
+        qt = item % a.n_qtiles;
+    }
 
     const int32_t* plan = a.plan;
     const int nq = plan[4];
@@ -489,6 +497,55 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
         }
     }
     store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, c);
+}
+
+// ---------------------------------------------------------------- tile order
+// Query tiles of a dynamic-threshold plan carry very different numbers of keys.  Workgroups
+// start in grid order, so the tile kernel takes its (tile, head) items longest first (list
+// scheduling: the long ones do not end up in the last wave of workgroups).  One workgroup sums
+// each tile's span lengths and sorts the tiles by that count, descending, lower tile first on
+// ties (bitonic sort of (count + 1, ~tile) keys in LDS).  A plan that does not belong to the
+// call gives the plan order; the tile kernel rejects its items itself.
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(const int32_t* plan, int32_t nq, int32_t* order) {
+    __shared__ unsigned long long key[kMaxTiles];
+    const int tid = threadIdx.x;
+    const bool ok = plan[0] == (int32_t)VDIT_PLAN_MAGIC && plan[4] == nq && nq <= kMaxTiles;
+    const int n_spans = ok ? plan[5] : 0;
+    const int32_t* row_ptr = plan + VDIT_PLAN_HEADER_WORDS + 2 * nq;
+    const int32_t* spans = row_ptr + nq + 1;
+    int P = 1;
+    while (P < nq) P <<= 1;
+    for (int t = tid; t < P; t += kOrderThreads) {
+        unsigned long long k = 0;  // padding sorts last
+        if (t < nq) {
+            long long n = 0;
+            if (ok) {
+                const int b = row_ptr[t], e = row_ptr[t + 1];
+                if (0 <= b && b <= e && e <= n_spans)
+                    for (int sp = b; sp < e; ++sp) n += max(spans[2 * sp + 1], 0);
+            }
+            n = min(n, (long long)0x7ffffffe);
+            k = ((unsigned long long)(n + 1) << 32) | (0xffffffffu - (unsigned)t);
+        }
+        key[t] = k;
+    }
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P; i += kOrderThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned long long x = key[i], y = key[ixj];
+                    if ((i & k) == 0 ? x < y : x > y) {  // descending overall
+                        key[i] = y;
+                        key[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    for (int t = tid; t < nq; t += kOrderThreads) order[t] = (int32_t)(0xffffffffu - (unsigned)(key[t] & 0xffffffffu));
 }
 
 // ---------------------------------------------------------------- unit kernel
@@ -885,6 +942,8 @@ struct Workspace {
     size_t cnt_words = 0;
     float* part = nullptr;
     size_t part_floats = 0;
+    int32_t* order = nullptr;  // tile kernel order (rewritten by every call that uses it)
+    size_t order_words = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
@@ -955,9 +1014,28 @@ hipError_t launch_unit(AttnArgs a, int n_heads_tiles, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t order_workspace(hipStream_t s, size_t words, int32_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[{dev, s}];
+    if ((e = grow(w.order, w.order_words, words, false, s)) != hipSuccess) return e;
+    *out = w.order;
+    return hipSuccess;
+}
+
 template <int D, bool QF, bool OF>
-hipError_t launch_tile(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_tile(AttnArgs a, bool longest_first, hipStream_t s) {
     const unsigned blocks = (unsigned)(a.n_qtiles * a.heads);
+    a.order = nullptr;
+    if (longest_first) {
+        int32_t* order = nullptr;
+        hipError_t e = order_workspace(s, (size_t)a.n_qtiles, &order);
+        if (e != hipSuccess) return e;
+        tile_order_kernel<<<1, kOrderThreads, 0, s>>>(a.plan, a.n_qtiles, order);
+        a.order = order;
+    }
     attn_tile_kernel<D, QF, OF><<<blocks, kTileWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -966,7 +1044,7 @@ template <int D, bool QF, bool OF>
 hipError_t launch_k(const AttnLaunch& L, const AttnArgs& a, hipStream_t s) {
     // neighbouring log-radial tiles (and tiles of dynamic plans) do not share span lists:
     // one tile per workgroup
-    if (is_radial(L.mask_kind) || L.unpaired) return launch_tile<D, QF, OF>(a, s);
+    if (is_radial(L.mask_kind) || L.unpaired) return launch_tile<D, QF, OF>(a, L.unpaired, s);
     return launch_unit<D, QF, OF>(a, L.n_qtiles * L.heads, s);
 }
 
