@@ -261,10 +261,11 @@ int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vd
  * bf16 before the P.V product.  A query tile's keys may be split over several workgroups,
  * whose partial results are merged in a fixed order: outputs are deterministic for a given
  * device.
- * Memory: for CHUNK_CAUSAL and DENSE static plans the library keeps a workspace per (device, stream),
- * allocated (hipMalloc, with a device synchronisation) on the first call that needs more and
- * kept until the process ends: per-tile counters (4 bytes per head and query tile) and
- * partial results (two 135 KB slots per CU for head_dim 128).  Calls on one stream are ordered;
+ * Memory: the library keeps a workspace per (device, stream), allocated (hipMalloc, with a
+ * device synchronisation) on the first call that needs more and kept until the process ends.
+ * For CHUNK_CAUSAL and DENSE static plans it holds per-tile counters (4 bytes per head and
+ * query tile) and partial results (two 135 KB slots per CU for head_dim 128); for dynamic
+ * plans, the order of the query tiles (4 bytes per tile; tiles with more keys run first).  Calls on one stream are ordered;
  * calls that may run at the same time must use different streams.
  * Errors: head counts or head_dim differing from the cache's, head_dim not 64 or 128 ->
  * INVALID_ARG / UNSUPPORTED; more than 4096 query tiles in one call -> UNSUPPORTED (split the
