@@ -220,10 +220,14 @@ __global__ __launch_bounds__(kPThreads, 1) void qkv_rope_append_kernel(ProjArgs 
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the next stage must have landed; the one after it may still be in flight
+        // the next stage must have landed; the one after it may still be in flight.  A plain
+        // barrier: __syncthreads() would add a fence, which waits for every load in flight
+        // (vmcnt 0), the DMA of the stage two ahead included.  No fence is needed: each wave's
+        // own DMA is complete at its wait, and the fragment reads of this step were consumed
+        // by its MFMAs before the barrier.
         if (kk + 2 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        asm volatile("s_barrier" ::: "memory");
         st = st == 2 ? 0 : st + 1;
     }
 
