@@ -11,7 +11,9 @@ before the timed region.
 in place of the static one; the step then carries that plan's four launches.
 
 Prints one JSON line.  value = attention FLOP on computed blocks / step time (TFLOP/s);
-the attention kernel alone is timed with HIP events on its launch stream.
+the attention kernel alone is timed with HIP events on its launch stream (mean and median
+over the timed steps, warm caches), and again over --cold-steps steps each preceded by a
+512 MiB scratch write that evicts the MALL and the L2s (cold: K/V, Q and plan from HBM).
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def parse():
                     help="time the fused QKV projection + RoPE + K/V append of the Wan-1.3B chunk")
     ap.add_argument("--rel-l1", action="store_true",
                     help="time the block-reuse indicator (relative L1 of 30 blocks of 4680 x 1536 bf16 features)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="attention calls timed after a 512 MiB scratch write each (cold MALL and L2); 0: skip")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one device-to-device copy of MIB MiB before timing (HBM counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -345,9 +349,23 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    attn_avg = sum(b.elapsed_time(c) for _, b, c in events) / args.steps
+    attn_times = [b.elapsed_time(c) for _, b, c in events]
+    attn_avg = sum(attn_times) / args.steps
     plan_avg = sum(a.elapsed_time(b) for a, b, _ in events) / args.steps
     attn_tflops = flop / (attn_avg * 1e-3) / 1e12
+
+    # cold: before each step, a 512 MiB write evicts the 256 MB MALL and the L2s, so the step
+    # reads its K/V, Q and plan from HBM (the scratch write is outside the timed events)
+    cold = []
+    if args.cold_steps > 0:
+        scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.int32, device="cuda")
+        cev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            scratch.fill_(i)
+            step(cev[i])
+        torch.cuda.synchronize()
+        cold = [b.elapsed_time(c) for _, b, c in cev]
+        del scratch
 
     traffic = traffic_per_launch()
     result = {
@@ -370,6 +388,8 @@ def main():
                    "computed_block_flop": flop, "plan": "static" if tau is None else f"dynamic tau={tau}"},
         "plan_ms_per_chunk": round(plan_avg, 4),
         "attn_ms_per_chunk": round(attn_avg, 4),
+        "attn_ms_per_chunk_median": round(float(np.median(attn_times)), 4),
+        "attn_ms_per_chunk_cold": round(float(np.median(cold)), 4) if cold else None,
         "attn_tflops": round(attn_tflops, 2),
         "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -130,7 +130,8 @@ def test_tau_one_equals_the_static_device_plan():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,tau", [("small_radial", 0.3), ("small_chunk_pad", 0.4), ("small_dense_d64", 0.5)])
+@pytest.mark.parametrize("name,tau", [("small_radial", 0.3), ("small_chunk_pad", 0.4), ("small_dense_d64", 0.5),
+                                      ("wan13b_chunk_h2", 0.3)])
 def test_attention_on_a_dynamic_plan(name, tau):
     """Attention with the flagged mask on the device's dynamic plan equals the oracle's masked
     attention over exactly the keys the plan keeps."""
