@@ -72,10 +72,11 @@ __global__ void rope_inplace_kernel(RopeDev r, int32_t n, int32_t hw, int32_t wi
 }
 
 // ---- KV append.  Block = 64 tokens x one head.  Every thread issues all its global loads
-// before its first store (the compiler cannot move a load above a possibly aliasing store).
-// Keys: rotated (optional) and written to k[h][phys][:].  Values: staged in LDS by token
-// rows and written transposed to v[h][d][phys], consecutive lanes writing consecutive keys
-// of one channel row.
+// (K and V, then the RoPE (cos, sin) of its pairs) before its first store (the compiler
+// cannot move a load above a possibly aliasing store).  Keys: rotated (optional) and written
+// to k[h][phys][:].  Values: staged in LDS by token rows and written transposed to
+// v[h][d][phys], 16 bytes (8 consecutive keys of one channel row) per lane where the 8 keys
+// are consecutive in the ring (one frame, frames a multiple of 8 tokens), else key by key.
 constexpr int kAppendTok = 64;
 
 template <int D, bool F32>
@@ -89,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
     constexpr int CH = D / 8;
     constexpr int PER = kAppendTok * CH / kThreads;  // chunks per thread
     constexpr int PITCH = D + 2;                     // bf16 elements per LDS row, odd dword count per row
+    constexpr int VT_ITEMS = D * (kAppendTok / 8) / kThreads;  // (channel, 8-key group) items per thread
     __shared__ uint16_t sv[kAppendTok * PITCH];
     const int32_t h = blockIdx.y;
     const int32_t n0 = blockIdx.x * kAppendTok;
@@ -106,6 +108,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
             load8<F32>(v, (int64_t)tok * v_st + (int64_t)h * v_sh + ch * 8, xv[i]);
         }
     }
+    float2 cs[PER][4];
+    if (has_rope) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + i * kThreads;
+            const int32_t tok = min(n0 + c / CH, n - 1), ch = c % CH;
+            const int32_t f = tok / hw, s = tok % hw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cs[i][e] = rope_cs(r, ch * 4 + e, t0 + f, s / width, s % width);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int c = tid + i * kThreads;
@@ -113,7 +126,10 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
         if (tok >= n) continue;
         const int32_t f = tok / hw, s = tok % hw;
         const int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
-        if (has_rope) rope_rotate8(r, ch * 4, t0 + f, s / width, s % width, xk[i]);
+        if (has_rope) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rope_apply(cs[i][e], xk[i][2 * e], xk[i][2 * e + 1]);
+        }
         *reinterpret_cast<u32x4*>(kc + ((int64_t)h * kv_rows + phys) * D + ch * 8) = pack_bf16x8(xk[i]);
         const u32x4 pv = pack_bf16x8(xv[i]);
         uint16_t* row = sv + lt * PITCH + ch * 8;
@@ -122,12 +138,31 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
         for (int e = 0; e < 8; ++e) row[e] = src[e];
     }
     __syncthreads();
-    const int lane = tid & 63, wave = tid >> 6;
-    const int32_t tok = n0 + lane;
-    if (tok < n) {
-        const int32_t f = tok / hw, s = tok % hw;
-        const int64_t phys = (int64_t)((t0 + f) % capacity) * frame_stride + s;
-        for (int d = wave; d < D; d += kThreads / 64) vt[((int64_t)h * D + d) * kv_rows + phys] = sv[lane * PITCH + d];
+    // item = (channel d, keys 8 g .. 8 g + 7 of the block); eight 2-byte LDS reads down a column
+    // (rows 65 dwords apart: the lanes of a read hit distinct banks)
+#pragma unroll
+    for (int it = 0; it < VT_ITEMS; ++it) {
+        const int j = tid + it * kThreads;
+        const int d = j >> 3, g8 = j & 7;
+        const int32_t tok0 = n0 + 8 * g8;
+        if (tok0 >= n) continue;
+        uint16_t e16[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e16[u] = sv[(8 * g8 + u) * PITCH + d];
+        uint16_t* row = vt + ((int64_t)h * D + d) * kv_rows;
+        const int32_t f0 = tok0 / hw, s0 = tok0 % hw;
+        if ((hw & 7) == 0 && tok0 + 8 <= n) {  // 8 keys of one frame, 16-byte aligned in the ring
+            const int64_t phys0 = (int64_t)((t0 + f0) % capacity) * frame_stride + s0;
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = (uint32_t)e16[2 * q] | ((uint32_t)e16[2 * q + 1] << 16);
+            *reinterpret_cast<u32x4*>(row + phys0) = w;
+        } else {
+            for (int u = 0; u < 8 && tok0 + u < n; ++u) {
+                const int32_t tu = tok0 + u, fu = tu / hw, su = tu % hw;
+                row[(int64_t)((t0 + fu) % capacity) * frame_stride + su] = e16[u];
+            }
+        }
     }
 }
 
