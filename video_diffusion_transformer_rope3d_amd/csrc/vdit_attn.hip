@@ -503,50 +503,42 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
 // ---------------------------------------------------------------- tile order
 // Query tiles of a dynamic-threshold plan carry very different numbers of keys.  Workgroups
 // start in grid order, so the tile kernel takes its (tile, head) items longest first (list
-// scheduling: the long ones do not end up in the last wave of workgroups).  One workgroup sums
-// each tile's span lengths and sorts the tiles by that count, descending, lower tile first on
-// ties (bitonic sort of (count + 1, ~tile) keys in LDS).  A plan that does not belong to the
-// call gives the plan order; the tile kernel rejects its items itself.
+// scheduling: the long ones do not end up in the last wave of workgroups).  One workgroup
+// sums each tile's span lengths (a wave per tile) and ranks the tiles by (count, lower tile
+// first): a tile's rank is the number of tiles ahead of it, read from LDS by every thread in
+// step (broadcast reads, no barriers).  A plan that does not belong to the call gives the
+// plan order; the tile kernel rejects its items itself.
 constexpr int kOrderThreads = 1024;
 __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(const int32_t* plan, int32_t nq, int32_t* order) {
-    __shared__ unsigned long long key[kMaxTiles];
+    __shared__ int32_t s_rp[kMaxTiles + 1];
+    __shared__ int32_t s_cnt[kMaxTiles];
     const int tid = threadIdx.x;
     const bool ok = plan[0] == (int32_t)VDIT_PLAN_MAGIC && plan[4] == nq && nq <= kMaxTiles;
     const int n_spans = ok ? plan[5] : 0;
     const int32_t* row_ptr = plan + VDIT_PLAN_HEADER_WORDS + 2 * nq;
     const int32_t* spans = row_ptr + nq + 1;
-    int P = 1;
-    while (P < nq) P <<= 1;
-    for (int t = tid; t < P; t += kOrderThreads) {
-        unsigned long long k = 0;  // padding sorts last
-        if (t < nq) {
-            long long n = 0;
-            if (ok) {
-                const int b = row_ptr[t], e = row_ptr[t + 1];
-                if (0 <= b && b <= e && e <= n_spans)
-                    for (int sp = b; sp < e; ++sp) n += max(spans[2 * sp + 1], 0);
-            }
-            n = min(n, (long long)0x7ffffffe);
-            k = ((unsigned long long)(n + 1) << 32) | (0xffffffffu - (unsigned)t);
-        }
-        key[t] = k;
+    for (int t = tid; t <= nq; t += kOrderThreads) s_rp[t] = ok ? row_ptr[t] : 0;
+    __syncthreads();
+    // one wave per tile: lanes stride over the tile's spans, a shuffle tree adds them
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int t = wave; t < nq; t += kOrderThreads / 64) {
+        const int b = max(s_rp[t], 0), e = min(s_rp[t + 1], n_spans);
+        int n = 0;
+        for (int sp = b + lane; sp < e; sp += 64) n += max(spans[2 * sp + 1], 0);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+        if (lane == 0) s_cnt[t] = n;
     }
     __syncthreads();
-    for (int k = 2; k <= P; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < P; i += kOrderThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const unsigned long long x = key[i], y = key[ixj];
-                    if ((i & k) == 0 ? x < y : x > y) {  // descending overall
-                        key[i] = y;
-                        key[ixj] = x;
-                    }
-                }
-            }
-            __syncthreads();
+    for (int t = tid; t < nq; t += kOrderThreads) {
+        const unsigned c = (unsigned)s_cnt[t];
+        int rank = 0;
+        for (int u = 0; u < nq; ++u) {
+            const unsigned cu = (unsigned)s_cnt[u];
+            rank += cu > c || (cu == c && u < t);
         }
-    for (int t = tid; t < nq; t += kOrderThreads) order[t] = (int32_t)(0xffffffffu - (unsigned)(key[t] & 0xffffffffu));
+        order[rank] = t;
+    }
 }
 
 // ---------------------------------------------------------------- unit kernel
