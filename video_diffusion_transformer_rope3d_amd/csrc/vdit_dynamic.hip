@@ -87,12 +87,10 @@ __device__ inline float reduce_rows(float* red, const float (&acc)[8]) {
 // Mean of the rotated queries of query tile i, head h.  Each thread loads 16 or 32 bytes
 // (eight channels) of a row per step; D/8 threads cover a row.
 template <int D, bool QF32>
-__global__ __launch_bounds__(kDynThreads) void dyn_pool_q_kernel(PlanGeom g, const void* q, int64_t q_st,
-                                                                 int64_t q_sh, RopeDev r, bool has_rope,
-                                                                 int32_t width, float* qbar) {
+__device__ __forceinline__ void pool_q_tile(float* red, int i, PlanGeom g, const void* q, int64_t q_st, int64_t q_sh,
+                                            RopeDev r, bool has_rope, int32_t width, float* qbar) {
     constexpr int LPR = D / 8, RPS = kDynThreads / LPR;
-    __shared__ float red[RPS * D];
-    const int i = blockIdx.x, h = blockIdx.y, heads = gridDim.y, t = threadIdx.x;
+    const int h = blockIdx.y, heads = gridDim.y, t = threadIdx.x;
     const QTile qt = plan_qtile(g, i);
     const int c0 = (t % LPR) * 8;
     PairTab pt[4];
@@ -124,12 +122,10 @@ __global__ __launch_bounds__(kDynThreads) void dyn_pool_q_kernel(PlanGeom g, con
 // Mean of the cached (rotated) keys of key tile j = slot * tiles_per_frame + piece, head h,
 // written transposed: kbar_t[(h * D + d) * nk + j]; empty slots give zeros.
 template <int D>
-__global__ __launch_bounds__(kDynThreads) void dyn_pool_k_kernel(PlanGeom g, const int32_t* slot_frame,
-                                                                 const uint16_t* kc, int64_t kv_rows, int32_t nk,
-                                                                 float* kbar_t) {
+__device__ __forceinline__ void pool_k_tile(float* red, int j, PlanGeom g, const int32_t* slot_frame,
+                                            const uint16_t* kc, int64_t kv_rows, int32_t nk, float* kbar_t) {
     constexpr int LPR = D / 8, RPS = kDynThreads / LPR;
-    __shared__ float red[RPS * D];
-    const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int h = blockIdx.y, t = threadIdx.x;
     const int tpf = ceil_div(g.hw, g.tile);
     const int slot = j / tpf, s0 = (j - slot * tpf) * g.tile;
     const int len = min(g.tile, g.hw - s0);
@@ -147,6 +143,20 @@ __global__ __launch_bounds__(kDynThreads) void dyn_pool_k_kernel(PlanGeom g, con
     }
     const float sum = reduce_rows<D>(red, acc);
     if (t < D) kbar_t[((size_t)h * D + t) * nk + j] = sum * (1.f / (float)len);
+}
+
+// Both poolings in one launch (they are independent): workgroups [0, nq) pool query tiles,
+// [nq, nq + nk) key tiles.
+template <int D, bool QF32>
+__global__ __launch_bounds__(kDynThreads) void dyn_pool_kernel(PlanGeom g, const void* q, int64_t q_st, int64_t q_sh,
+                                                               RopeDev r, bool has_rope, int32_t width, float* qbar,
+                                                               int32_t nq, const int32_t* slot_frame,
+                                                               const uint16_t* kc, int64_t kv_rows, int32_t nk,
+                                                               float* kbar_t) {
+    __shared__ float red[(kDynThreads / (D / 8)) * D];
+    const int b = blockIdx.x;
+    if (b < nq) pool_q_tile<D, QF32>(red, b, g, q, q_st, q_sh, r, has_rope, width, qbar);
+    else pool_k_tile<D>(red, b - nq, g, slot_frame, kc, kv_rows, nk, kbar_t);
 }
 
 // Partial proxies over the channel range [z * cps, (z + 1) * cps) of grid slice z, for 16
@@ -479,14 +489,15 @@ hipError_t launch_dyn_d(const DynLaunch& L, hipStream_t s) {
     float* prox = L.proxies ? L.proxies : reinterpret_cast<float*>(take(b_prox));
     int32_t* runs = reinterpret_cast<int32_t*>(take(b_runs));
     long long* pairs = reinterpret_cast<long long*>(take(b_pairs));
+    const uint16_t* kc = static_cast<const uint16_t*>(L.kc);
     if (L.q.dtype == VDIT_DTYPE_FP32)
-        dyn_pool_q_kernel<D, true><<<dim3(nq, heads), kDynThreads, 0, s>>>(
-            g, L.q.data, L.q.stride_token, L.q.stride_head, L.rope, L.has_rope, L.width, qbar);
+        dyn_pool_kernel<D, true><<<dim3(nq + nk, heads), kDynThreads, 0, s>>>(
+            g, L.q.data, L.q.stride_token, L.q.stride_head, L.rope, L.has_rope, L.width, qbar, nq, L.slot_frame, kc,
+            L.kv_rows, nk, kbar_t);
     else
-        dyn_pool_q_kernel<D, false><<<dim3(nq, heads), kDynThreads, 0, s>>>(
-            g, L.q.data, L.q.stride_token, L.q.stride_head, L.rope, L.has_rope, L.width, qbar);
-    dyn_pool_k_kernel<D><<<dim3(nk, heads), kDynThreads, 0, s>>>(g, L.slot_frame, static_cast<const uint16_t*>(L.kc),
-                                                                   L.kv_rows, nk, kbar_t);
+        dyn_pool_kernel<D, false><<<dim3(nq + nk, heads), kDynThreads, 0, s>>>(
+            g, L.q.data, L.q.stride_token, L.q.stride_head, L.rope, L.has_rope, L.width, qbar, nq, L.slot_frame, kc,
+            L.kv_rows, nk, kbar_t);
     dyn_score_kernel<<<dim3(ceil_div(nk, kScoreK), ceil_div(nq, kScoreQ), slices), kDynThreads, 0, s>>>(
         qbar, kbar_t, hd, cps, nq, nk, part);
     dyn_count_kernel<<<nq, kDynThreads, 0, s>>>(g, L.slot_frame, part, slices, nq, nk, L.scale, L.keep_frac, prox,
