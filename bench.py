@@ -6,6 +6,7 @@ attention forward with RoPE applied to Q while it is loaded.  Inputs are residen
 before the timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--dynamic-tau TAU] [--no-cpu-baseline]
+                    [--library-reference]
 
 --dynamic-tau builds the content-adaptive plan (pooled tile logits, adaptive threshold)
 in place of the static one; the step then carries that plan's four launches.
@@ -14,6 +15,8 @@ Prints one JSON line.  value = attention FLOP on computed blocks / step time (TF
 the attention kernel alone is timed with HIP events on its launch stream (mean and median
 over the timed steps, warm caches), and again over --cold-steps steps each preceded by a
 512 MiB scratch write that evicts the MALL and the L2s (cold: K/V, Q and plan from HBM).
+--library-reference adds the stock library call on the same shapes (torch's SDPA where every
+query sees every cached key; F.linear with --qkv) as context, timed the same way.
 """
 from __future__ import annotations
 
@@ -57,6 +60,9 @@ def parse():
                     help="run one device-to-device copy of MIB MiB before timing (HBM counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="offline: turn two rocprofv3 counter_collection CSVs into profiles/attn_fwd_traffic.json")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="also time the stock library call for the same shapes: torch's SDPA (all keys visible "
+                         "to every query only) or, with --qkv, the plain bf16 GEMM of F.linear")
     ap.add_argument("--traffic-copy-mib", type=int, default=256)
     ap.add_argument("--traffic-command", default="")
     return ap.parse_args()
@@ -104,6 +110,42 @@ def cpu_baseline(w, inputs, seconds):
                 sample=f"{heads} head passes ({w.heads} heads per chunk), each all {w.n_q} query rows against "
                        f"{len(st.k_phys)} cached keys: RoPE of Q, element mask, fp64 masked softmax attention "
                        f"({spent:.1f} s); the ring build (K rotation of all heads) is excluded")
+
+
+def time_library(fn, steps, warmup):
+    """Median ms of fn() over `steps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def library_attention(heads, n_q, n_k, head_dim, flop, steps, warmup):
+    """torch's scaled_dot_product_attention (ROCm flash backend) on random bf16 Q, K, V of
+    the workload's shapes with no mask: the same FLOP as the chunk when every query sees
+    every cached key."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    g = torch.Generator(device="cuda").manual_seed(1)
+    q = torch.randn((1, heads, n_q, head_dim), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn((1, heads, n_k, head_dim), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((1, heads, n_k, head_dim), device="cuda", generator=g).to(torch.bfloat16)
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+        ms = time_library(lambda: F.scaled_dot_product_attention(q, k, v), steps, warmup)
+    return {"call": "torch.nn.functional.scaled_dot_product_attention (flash backend), bf16, no mask",
+            "ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}
 
 
 def write_traffic(fetch_csv, write_csv, copy_mib, command):
@@ -253,6 +295,12 @@ def bench_qkv(args):
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "cpu_baseline": cpu,
     }
+    if args.library_reference:
+        import torch.nn.functional as F
+        lms = time_library(lambda: F.linear(x, w), args.steps, args.warmup)
+        result["library_reference"] = {"call": "torch.nn.functional.linear (bf16 GEMM alone: no bias, RoPE or "
+                                               "cache write)", "ms": round(lms, 4),
+                                       "tflops": round(flop / (lms * 1e-3) / 1e12, 2)}
     print(json.dumps(result), flush=True)
 
 
@@ -396,6 +444,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
+    if args.library_reference:
+        n_k = int((s.cache.slot_host >= 0).sum()) * w.tokens_per_frame  # keys of the valid slots
+        if n_k and pairs == w.n_q * n_k:
+            result["library_reference"] = library_attention(w.heads, w.n_q, n_k, w.head_dim, flop, args.steps,
+                                                             args.warmup)
+        else:
+            result["library_reference"] = None  # masked: no stock call computes the same blocks
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
