@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from workloads import get_workload, make_inputs
+from video_diffusion_transformer_rope3d_amd import AttentionSession
 from video_diffusion_transformer_rope3d_amd import binding as B
 
 from harness import compare, device_plan_words, run_workload, sample_rows, session_for, to_dev, torch_dtype
@@ -59,6 +60,39 @@ def test_device_plan_bit_exact(name):
     np.testing.assert_array_equal(dev, host)
     if want is not None:
         np.testing.assert_array_equal(dev, want)
+
+
+# Geometries past the device builder's LDS tables (more than 2048 query tiles, more than
+# 16384 (tile, slot) pairs, frames of more than 65535 tokens) and one that fits them but
+# needs two rounds of 1024 tiles.  Slot tables are written directly (frames with holes and
+# out-of-order slots); no K/V data is needed for a plan.
+PLAN_GEOMETRIES = [
+    # name, mask kind, chunk frames, frame h, w, capacity, query frames, query t0
+    ("pairs_over_table", "log_radial", 1, 16, 20, 128, 64, 40),
+    ("tiles_over_table", "dense", 1, 64, 64, 66, 65, 3),
+    ("frame_over_16_bits", "chunk_causal", 2, 256, 257, 3, 2, 4),
+    ("two_rounds_in_table", "dense", 1, 96, 96, 15, 15, 0),
+    ("two_rounds_chunks", "chunk_causal", 3, 96, 96, 15, 15, 2),
+]
+
+
+@pytest.mark.parametrize("geom", PLAN_GEOMETRIES, ids=[g[0] for g in PLAN_GEOMETRIES])
+def test_device_plan_large_geometry_equals_host(geom):
+    name, kind, cf, fh, fw, cap, qf, qt0 = geom
+    _print("device plan geometry", name)
+    s = AttentionSession(1, 64, fh, fw, cap, (24, 20, 20), 1e4, max_t=qt0 + qf + cap + 4, mask=kind,
+                         chunk_frames=cf)
+    rng = np.random.default_rng(len(name))
+    table = np.arange(qt0 + qf - cap, qt0 + qf, dtype=np.int32)  # the newest cap frames
+    table = np.where(table < 0, -1, table)
+    rng.shuffle(table)
+    table[rng.random(cap) < 0.2] = -1  # holes
+    s.cache.slot_host[:] = table
+    s.cache.slot_dev.copy_(torch.from_numpy(table))
+    dev = device_plan_words(s.plan(qf, qt0, B.VDIT_WHERE_DEVICE))
+    host = s.plan(qf, qt0, B.VDIT_WHERE_HOST)
+    assert int(host[4]) > 0 and int(host[5]) > 0
+    np.testing.assert_array_equal(dev, host)
 
 
 # ------------------------------------------------------------------ RoPE and the cache

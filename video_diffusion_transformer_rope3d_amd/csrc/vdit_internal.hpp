@@ -86,6 +86,18 @@ struct QTile {
 
 __host__ __device__ inline QTile plan_qtile(const PlanGeom& g, int32_t i) {
     QTile qt{0, 0, 0, 0, 0};
+    if (is_radial(g.kind) && g.frames > 0) {  // every unit is one whole frame: same tile count
+        const int32_t nt = ceil_div(g.hw, g.tile);
+        const int32_t u = i / nt;
+        if (i < 0 || u >= g.frames) return qt;
+        const int32_t off = (i - u * nt) * g.tile;
+        qt.q_start = u * g.hw + off;
+        qt.q_len = (g.hw - off) < g.tile ? (g.hw - off) : g.tile;
+        qt.unit_first_frame = u;
+        qt.t_q = g.t0 + u + off / g.hw;
+        qt.piece = i - u * nt;
+        return qt;
+    }
     int32_t nu = plan_units(g);
     for (int32_t u = 0; u < nu; ++u) {
         int32_t fb, fe;
@@ -141,15 +153,15 @@ __host__ __device__ inline bool plan_slot_range(const PlanGeom& g, const QTile& 
     return *b > *a;
 }
 
-// Emits the maximal ascending runs of visible physical key indices of query tile qt.
-template <class Emit>
-__host__ __device__ inline void plan_tile_spans(const PlanGeom& g, const int32_t* slot_frame, const QTile& qt,
-                                                Emit&& emit) {
+// Merges the per-slot key ranges (range(slot, &a, &b): within-frame [a, b), false when the
+// slot contributes nothing) into maximal ascending runs of physical key indices.
+template <class Range, class Emit>
+__host__ __device__ inline void plan_runs(int32_t capacity, int32_t frame_stride, Range&& range, Emit&& emit) {
     int32_t run_start = 0, run_end = -1;
-    for (int32_t slot = 0; slot < g.capacity; ++slot) {
+    for (int32_t slot = 0; slot < capacity; ++slot) {
         int32_t a, b;
-        if (!plan_slot_range(g, qt, slot_frame[slot], &a, &b)) continue;
-        int32_t s0 = slot * g.frame_stride + a, s1 = slot * g.frame_stride + b;
+        if (!range(slot, &a, &b)) continue;
+        int32_t s0 = slot * frame_stride + a, s1 = slot * frame_stride + b;
         if (s0 == run_end) {
             run_end = s1;
         } else {
@@ -159,6 +171,16 @@ __host__ __device__ inline void plan_tile_spans(const PlanGeom& g, const int32_t
         }
     }
     if (run_end >= 0) emit(run_start, run_end - run_start);
+}
+
+// Emits the maximal ascending runs of visible physical key indices of query tile qt.
+template <class Emit>
+__host__ __device__ inline void plan_tile_spans(const PlanGeom& g, const int32_t* slot_frame, const QTile& qt,
+                                                Emit&& emit) {
+    plan_runs(
+        g.capacity, g.frame_stride,
+        [&](int32_t slot, int32_t* a, int32_t* b) { return plan_slot_range(g, qt, slot_frame[slot], a, b); },
+        emit);
 }
 
 __host__ __device__ inline size_t plan_bound_words(int32_t n_qtiles, int32_t capacity) {

@@ -180,62 +180,127 @@ __global__ void kv_zero_pad_kernel(int32_t hw, int32_t frame_stride, int32_t t0,
     }
 }
 
-// ---- device plan builder: one wave.  Lane i of round r takes query tile 64 r + i: counts
-// its spans, a shuffle scan turns counts into row pointers, then it writes its spans.  All
-// integer, so the words equal the host builder's.
-constexpr int kPlanThreads = 64;
+// ---- device plan builder: one workgroup of 1024 threads.
+// 1. Every tile's geometry (LDS) and its qtile words; the slot table into LDS.
+// 2. One thread per (tile, slot) pair: the slot's within-frame key range for the tile,
+//    packed into LDS (the divisions of the visibility rule run in parallel here).
+// 3. Rounds of 1024 tiles, a thread per tile: it merges its slots' ranges into runs and
+//    counts them, a block scan turns the counts into row pointers, then it writes its spans.
+// Plans too large for the LDS tables take the same rounds with the ranges computed inline.
+// All integer, with the host builder's merge (plan_runs), so the words equal the host's.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanMaxSlots = 1024;
+constexpr int kPlanMaxTiles = 2048;
+constexpr int kPlanPairWords = 16384;
+constexpr uint32_t kPlanNoRange = 0xFFFFFFFFu;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_build_kernel(PlanGeom g, const int32_t* slot_frame, int32_t nq,
                                                                   int32_t* plan) {
-    __shared__ int32_t s_slot[1024];
-    const int lane = threadIdx.x;
-    const int32_t* sf = slot_frame;
-    if (g.capacity <= 1024) {
-        for (int i = lane; i < g.capacity; i += kPlanThreads) s_slot[i] = slot_frame[i];
-        sf = s_slot;
-    }
-    __syncthreads();
+    __shared__ int32_t s_slot[kPlanMaxSlots];
+    __shared__ uint32_t s_range[kPlanPairWords];  // (a | b << 16) of pair tile * capacity + slot
+    __shared__ int32_t s_tq[kPlanMaxTiles], s_piece[kPlanMaxTiles];
+    __shared__ int32_t s_wave[kPlanWaves];
+    __shared__ long long s_pairs[kPlanWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t cap = g.capacity;
+    const bool tables = cap <= kPlanMaxSlots && nq <= kPlanMaxTiles && (int64_t)nq * cap <= kPlanPairWords &&
+                        g.hw <= 0xFFFF;
     int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
     int32_t* row_ptr = qtiles + 2 * nq;
     int32_t* spans = row_ptr + nq + 1;
+
+    for (int32_t i = tid; i < nq; i += kPlanThreads) {
+        const QTile qt = plan_qtile(g, i);
+        qtiles[2 * i] = qt.q_start;
+        qtiles[2 * i + 1] = qt.q_len;
+        if (tables) {
+            s_tq[i] = qt.t_q;
+            s_piece[i] = qt.piece;
+        }
+    }
+    if (tables)
+        for (int32_t j = tid; j < cap; j += kPlanThreads) s_slot[j] = slot_frame[j];
+    __syncthreads();
+    if (tables) {
+        for (int32_t p = tid; p < nq * cap; p += kPlanThreads) {
+            const int32_t i = p / cap, j = p - i * cap;
+            const QTile qt{0, 0, s_tq[i], 0, s_piece[i]};
+            int32_t a, b;
+            s_range[p] = plan_slot_range(g, qt, s_slot[j], &a, &b) ? (uint32_t)a | ((uint32_t)b << 16) : kPlanNoRange;
+        }
+        __syncthreads();
+    }
+
+    // the spans of tile i, from the LDS table or computed inline
+    auto tile_runs = [&](int32_t i, const QTile& qt, auto&& emit) {
+        if (tables) {
+            const uint32_t* rr = s_range + i * cap;
+            plan_runs(
+                cap, g.frame_stride,
+                [&](int32_t slot, int32_t* a, int32_t* b) {
+                    const uint32_t r = rr[slot];
+                    *a = (int32_t)(r & 0xFFFFu);
+                    *b = (int32_t)(r >> 16);
+                    return r != kPlanNoRange;
+                },
+                emit);
+        } else {
+            plan_tile_spans(g, slot_frame, qt, emit);
+        }
+    };
+
     int32_t carry = 0;
     long long pairs = 0;
     for (int32_t base = 0; base < nq; base += kPlanThreads) {
-        const int32_t i = base + lane;
+        const int32_t i = base + tid;
         int32_t cnt = 0;
         QTile qt{0, 0, 0, 0, 0};
         if (i < nq) {
             qt = plan_qtile(g, i);
-            qtiles[2 * i] = qt.q_start;
-            qtiles[2 * i + 1] = qt.q_len;
             long long keys = 0;
-            plan_tile_spans(g, sf, qt, [&](int32_t, int32_t len) {
+            tile_runs(i, qt, [&](int32_t, int32_t len) {
                 ++cnt;
                 keys += len;
             });
             pairs += keys * qt.q_len;
         }
+        // block-wide inclusive scan of the counts: within the wave, then over the waves
         int32_t incl = cnt;
 #pragma unroll
-        for (int off = 1; off < kPlanThreads; off <<= 1) {
+        for (int off = 1; off < 64; off <<= 1) {
             const int32_t t = __shfl_up(incl, off);
             if (lane >= off) incl += t;
         }
+        if (lane == 63) s_wave[wave] = incl;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+        for (int w = 0; w < kPlanWaves; ++w) {
+            const int32_t v = s_wave[w];
+            before += w < wave ? v : 0;
+            total += v;
+        }
+        __syncthreads();  // s_wave is rewritten by the next round
+        incl += before;
         if (i < nq) {
             row_ptr[i + 1] = carry + incl;
             int32_t kk = carry + incl - cnt;
-            plan_tile_spans(g, sf, qt, [&](int32_t st, int32_t len) {
+            tile_runs(i, qt, [&](int32_t st, int32_t len) {
                 spans[2 * kk] = st;
                 spans[2 * kk + 1] = len;
                 ++kk;
             });
         }
-        carry += __shfl(incl, kPlanThreads - 1);
+        carry += total;
     }
 #pragma unroll
-    for (int off = kPlanThreads / 2; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
-    if (lane == 0) {
-        const unsigned long long tot = (unsigned long long)pairs;
+    for (int off = 32; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
+    if (lane == 0) s_pairs[wave] = pairs;
+    __syncthreads();
+    if (tid == 0) {
+        long long tot_pairs = 0;
+        for (int w = 0; w < kPlanWaves; ++w) tot_pairs += s_pairs[w];
+        const unsigned long long tot = (unsigned long long)tot_pairs;
         row_ptr[0] = 0;
         plan[0] = (int32_t)VDIT_PLAN_MAGIC;
         plan[1] = VDIT_PLAN_VERSION;
