@@ -1,15 +1,16 @@
 """Benchmark of one denoising-chunk attention step on one MI355X.
 
 A step is the whole hot path for one chunk: the chunk's K/V append into the ring cache
-(K rotated at global frames), the block plan built on the device, and the block-sparse
-attention forward with RoPE applied to Q while it is loaded.  Inputs are resident in HBM
-before the timed region.
+(K rotated at global frames), the block plan built on the device (by one extra workgroup of
+the append launch; --separate-plan: its own launch), and the block-sparse attention forward
+with RoPE applied to Q while it is loaded.  Inputs are resident in HBM before the timed
+region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--dynamic-tau TAU] [--no-cpu-baseline]
                     [--library-reference]
 
 --dynamic-tau builds the content-adaptive plan (pooled tile logits, adaptive threshold)
-in place of the static one; the step then carries that plan's four launches.
+in place of the static one; the step then carries the append and that plan's four launches.
 
 Prints one JSON line.  value = attention FLOP on computed blocks / step time (TFLOP/s);
 the attention kernel alone is timed with HIP events on its launch stream (mean and median
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--workload", default="wan13b_chunk")
     ap.add_argument("--dynamic-tau", type=float, default=None, metavar="TAU",
                     help="build the dynamic-threshold plan (tau in [0, 1]) instead of the static one")
+    ap.add_argument("--separate-plan", action="store_true",
+                    help="static plan from its own launch after the append (default: built in the append launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until reached)")
@@ -359,13 +362,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        s.append(k, v, w.q_t0)
         if ev is not None:
             ev[0].record(stream)
-        if tau is None:
+        if tau is not None:
+            s.append(k, v, w.q_t0)
+            s.plan_dynamic(q, w.q_frames, w.q_t0, tau, out=plan)
+        elif args.separate_plan:
+            s.append(k, v, w.q_t0)
             s.plan(w.q_frames, w.q_t0, out=plan)
         else:
-            s.plan_dynamic(q, w.q_frames, w.q_t0, tau, out=plan)
+            s.append_plan(k, v, w.q_t0, out=plan)
         if ev is not None:
             ev[1].record(stream)
         s.attend(q, w.q_frames, w.q_t0, plan, o=o, mask=mask)
@@ -399,7 +405,7 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     attn_times = [b.elapsed_time(c) for _, b, c in events]
     attn_avg = sum(attn_times) / args.steps
-    plan_avg = sum(a.elapsed_time(b) for a, b, _ in events) / args.steps
+    prep_avg = sum(a.elapsed_time(b) for a, b, _ in events) / args.steps
     attn_tflops = flop / (attn_avg * 1e-3) / 1e12
 
     # cold: before each step, a 512 MiB write evicts the 256 MB MALL and the L2s, so the step
@@ -433,8 +439,10 @@ def main():
                    "q_tokens": w.n_q, "kv_tokens": int(pairs // max(w.n_q, 1)) if m.kind != "log_radial" and tau is None else None,
                    "mean_keys_per_query": round(pairs / max(w.n_q, 1), 1),
                    "frame": f"{w.frame_h}x{w.frame_w}", "q_t0": w.q_t0, "mask": m.kind,
-                   "computed_block_flop": flop, "plan": "static" if tau is None else f"dynamic tau={tau}"},
-        "plan_ms_per_chunk": round(plan_avg, 4),
+                   "computed_block_flop": flop,
+                   "plan": (f"dynamic tau={tau}" if tau is not None else
+                            "static, separate launch" if args.separate_plan else "static, built in the append launch")},
+        "append_plan_ms_per_chunk": round(prep_avg, 4),
         "attn_ms_per_chunk": round(attn_avg, 4),
         "attn_ms_per_chunk_median": round(float(np.median(attn_times)), 4),
         "attn_ms_per_chunk_cold": round(float(np.median(cold)), 4) if cold else None,

@@ -213,6 +213,17 @@ int vdit_plan_bound(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, c
 int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
                    int32_t where, int32_t* plan_out, size_t cap_words, size_t* used_words, void* stream);
 
+/* vdit_kv_append_plan: vdit_kv_append(cache, rope, grid, t0, k, v, stream) followed by
+ * vdit_plan_mask(mask, grid, t0, cache, VDIT_WHERE_DEVICE, plan_dev, cap_words, used_words,
+ * stream): the device plan of the appended chunk as the query call, in one launch.  One
+ * extra workgroup builds the plan from the slot table with this append's frames in their
+ * slots, while the others append (two launches when capacity > 1024).  The cache contents,
+ * both slot tables and the plan words are those of the two calls.  Errors: those of the two
+ * calls, all checked before anything is launched. */
+int vdit_kv_append_plan(vdit_kv_cache* cache, const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0,
+                        vdit_tensor k, vdit_tensor v, const vdit_mask_cfg* mask, int32_t* plan_dev,
+                        size_t cap_words, size_t* used_words, void* stream);
+
 /* ---- dynamic-threshold block plan: "DynamicRad: Content-Adaptive Sparse Attention for
  * Long Video Diffusion", section 2, dual-mode strategy, mode 2 (pre-softmax attention logits
  * as importance proxies, an adaptive threshold inside the static rule's candidates).

@@ -206,6 +206,34 @@ def test_cache_and_append_errors(L):
     assert slots.tolist() == [-1, -1, -1]  # failed appends leave the slot table alone
 
 
+def test_append_plan_errors(L):
+    """The fused append + plan checks the arguments of both calls before anything runs."""
+    slots = np.full(3, -1, np.int32)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    desc = B.VditKVCache(fake, fake, fake, slots.ctypes.data, 3, 24, 2, 64)
+    t = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    g = B.grid(2, 4, 6)
+    m = B.mask_cfg("chunk_causal", 2)
+    n = ctypes.c_size_t(0)
+    assert L.vdit_plan_bound(ctypes.byref(m), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
+    used = ctypes.c_size_t(0)
+
+    def call(grid=g, t0=0, k=t, mask=m, plan=fake, cap=n.value):
+        mp = ctypes.byref(mask) if mask is not None else None
+        return L.vdit_kv_append_plan(ctypes.byref(desc), None, grid, t0, k, t, mp, plan, cap, ctypes.byref(used),
+                                     None)
+
+    assert call(mask=None) == B.VDIT_ERR_INVALID_ARG
+    assert call(plan=None) == B.VDIT_ERR_INVALID_ARG
+    assert call(cap=n.value - 1) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    assert call(grid=B.grid(4, 4, 6)) == B.VDIT_ERR_INVALID_ARG  # frames beyond capacity
+    assert call(t0=-1) == B.VDIT_ERR_INVALID_ARG
+    assert call(k=B.VditTensor(None, 0, 0, 128, 64)) == B.VDIT_ERR_INVALID_ARG
+    bad_tile = B.mask_cfg("chunk_causal", 2, tile=64)
+    assert call(mask=bad_tile) == B.VDIT_ERR_UNSUPPORTED
+    assert slots.tolist() == [-1, -1, -1]  # nothing appended
+
+
 def test_attention_errors(L):
     slots = np.array([0, 1, 2], np.int32)
     fake = 0x10000

@@ -95,6 +95,75 @@ def test_device_plan_large_geometry_equals_host(geom):
     np.testing.assert_array_equal(dev, host)
 
 
+def _assert_same_cache(a, b):
+    """Both slot tables equal, and the bits of K and V^T of every occupied slot (pad tokens
+    included); empty slots hold whatever the allocation held."""
+    np.testing.assert_array_equal(b.cache.slot_host, a.cache.slot_host)
+    assert torch.equal(b.cache.slot_dev, a.cache.slot_dev)
+    fs = a.cache.kv_rows // a.cache.desc.capacity
+    ka, kb = a.cache.k_view().view(torch.int16), b.cache.k_view().view(torch.int16)
+    va, vb = a.cache.v_view().view(torch.int16), b.cache.v_view().view(torch.int16)
+    for slot in np.flatnonzero(a.cache.slot_host >= 0).tolist():
+        r = slice(slot * fs, (slot + 1) * fs)
+        assert torch.equal(ka[:, r], kb[:, r]), f"K of slot {slot}"
+        assert torch.equal(va[:, :, r], vb[:, :, r]), f"V of slot {slot}"
+
+
+@pytest.mark.parametrize("name", SMALL + LARGE)
+def test_append_plan_equals_separate_calls(name):
+    """vdit_kv_append_plan: cache contents, both slot tables and plan words equal those of
+    vdit_kv_append then vdit_plan_mask; the plan also equals the host plan."""
+    _print("append + plan", name)
+    w = get_workload(name)
+    inp = make_inputs(w)
+    dt = torch_dtype(w)
+    a, b = session_for(w), session_for(w)
+    for t0, f, hk, hv in inp["history"]:
+        hk, hv = to_dev(hk, dt), to_dev(hv, dt)
+        a.append(hk, hv, t0)
+        b.append(hk, hv, t0)
+    k, v = to_dev(inp["k"], dt), to_dev(inp["v"], dt)
+    a.append(k, v, w.q_t0)
+    pa = a.plan(w.q_frames, w.q_t0)
+    pb = b.append_plan(k, v, w.q_t0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(device_plan_words(pb), device_plan_words(pa))
+    np.testing.assert_array_equal(device_plan_words(pb), b.plan(w.q_frames, w.q_t0, B.VDIT_WHERE_HOST))
+    _assert_same_cache(a, b)
+
+
+def test_append_plan_capacity_over_lds_table():
+    """Capacity 1100 (beyond the plan workgroup's 1024-slot table): the two-launch path."""
+    cap, fh, fw = 1100, 1, 8
+    a = AttentionSession(1, 64, fh, fw, cap, (24, 20, 20), 1e4, max_t=cap + 40, mask="chunk_causal", chunk_frames=3)
+    b = AttentionSession(1, 64, fh, fw, cap, (24, 20, 20), 1e4, max_t=cap + 40, mask="chunk_causal", chunk_frames=3)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    hist = torch.randn((cap * fh * fw, 1, 64), device="cuda", generator=g).to(torch.bfloat16)
+    a.append(hist, hist, 20)
+    b.append(hist, hist, 20)
+    k = torch.randn((4 * fh * fw, 1, 64), device="cuda", generator=g).to(torch.bfloat16)
+    a.append(k, k, cap + 20)
+    pa = a.plan(4, cap + 20)
+    pb = b.append_plan(k, k, cap + 20)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(device_plan_words(pb), device_plan_words(pa))
+    np.testing.assert_array_equal(device_plan_words(pb), b.plan(4, cap + 20, B.VDIT_WHERE_HOST))
+    _assert_same_cache(a, b)
+
+
+def test_append_of_more_frames_than_threads_updates_every_slot():
+    """One append of 300 frames (more than a workgroup's 256 threads) into a 300-slot ring:
+    the device slot table equals the host mirror and the oracle's ring."""
+    cap, fh, fw, t0 = 300, 2, 4, 17
+    s = AttentionSession(1, 64, fh, fw, cap, (24, 20, 20), 1e4, max_t=t0 + cap + 4, mask="dense")
+    z = torch.zeros((cap * fh * fw, 1, 64), dtype=torch.bfloat16, device="cuda")
+    s.append(z, z, t0)
+    ring = oracle.RingCache(cap, fh, fw, 1, 64)
+    ring.append(np.zeros((cap * fh * fw, 1, 64)), np.zeros((cap * fh * fw, 1, 64)), cap, t0, (24, 20, 20), 1e4)
+    np.testing.assert_array_equal(s.cache.slot_host, ring.slot_frame)
+    np.testing.assert_array_equal(s.cache.slot_dev.cpu().numpy(), ring.slot_frame)
+
+
 # ------------------------------------------------------------------ RoPE and the cache
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_rope_inplace_vs_oracle(dtype):

@@ -26,7 +26,7 @@ MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, 
 EXPORTS = (
     "vdit_abi_version", "vdit_last_error", "vdit_status_string", "vdit_token_positions",
     "vdit_rope_table_build", "vdit_rope3d_qk", "vdit_kv_cache_bytes", "vdit_kv_cache_reset",
-    "vdit_kv_append", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
+    "vdit_kv_append", "vdit_kv_append_plan", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
     "vdit_plan_dynamic", "vdit_block_attn_fwd", "vdit_block_rel_l1", "vdit_reuse_decide", "vdit_qkv_rope_append",
 )
 
@@ -98,6 +98,8 @@ def lib():
             "vdit_kv_cache_reset": (I32, [ctypes.POINTER(VditKVCache), P]),
             "vdit_kv_append": (I32, [ctypes.POINTER(VditKVCache), ctypes.POINTER(VditRopeCfg), VditGrid, I32,
                                      VditTensor, VditTensor, P]),
+            "vdit_kv_append_plan": (I32, [ctypes.POINTER(VditKVCache), ctypes.POINTER(VditRopeCfg), VditGrid, I32,
+                                          VditTensor, VditTensor, ctypes.POINTER(VditMaskCfg), P, SZ, pS, P]),
             "vdit_plan_qtiles": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(I32)]),
             "vdit_plan_bound": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(VditKVCache), pS]),
             "vdit_plan_mask": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32, ctypes.POINTER(VditKVCache), I32,
@@ -253,6 +255,20 @@ def vdit_kv_cache_reset(cache: KVCache, stream=None):
 def vdit_kv_append(cache: KVCache, rope, g: VditGrid, t0: int, k, v, stream=None):
     rp = ctypes.byref(rope.cfg) if rope is not None else None
     _check(lib().vdit_kv_append(ctypes.byref(cache.desc), rp, g, t0, tensor(k), tensor(v), _stream(stream)))
+
+
+def vdit_kv_append_plan(cache: KVCache, rope, g: VditGrid, t0: int, k, v, mask: VditMaskCfg, out=None,
+                        stream=None):
+    """Append of the chunk and the device plan of the same chunk as the query call, in one
+    launch; writes `out` (or a new int32 device tensor of the bound size) and returns it."""
+    import torch
+    bound = vdit_plan_bound(mask, g, t0, cache)
+    buf = torch.empty(bound, dtype=torch.int32, device="cuda") if out is None else out
+    rp = ctypes.byref(rope.cfg) if rope is not None else None
+    used = ctypes.c_size_t(0)
+    _check(lib().vdit_kv_append_plan(ctypes.byref(cache.desc), rp, g, t0, tensor(k), tensor(v), ctypes.byref(mask),
+                                     buf.data_ptr(), buf.numel(), ctypes.byref(used), _stream(stream)))
+    return buf
 
 
 def vdit_plan_qtiles(mask: VditMaskCfg, g: VditGrid, q_t0: int) -> int:

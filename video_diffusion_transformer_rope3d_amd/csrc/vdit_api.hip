@@ -164,6 +164,32 @@ int check_plan_args(const vdit_mask_cfg* mask, const vdit_grid& g, int32_t t0, c
     return VDIT_OK;
 }
 
+// Arguments of an append; fills *r (the rotation tables) when rope is given.
+int check_append(const vdit_kv_cache* c, const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0, vdit_tensor k,
+                 vdit_tensor v, RopeDev* r) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!c->k || !c->v || !c->slot_frame_dev || !c->slot_frame_host)
+        return fail(VDIT_ERR_INVALID_ARG, "cache buffers must be set");
+    if ((st = check_grid(grid))) return st;
+    if (grid.height * grid.width != c->tokens_per_frame)
+        return fail(VDIT_ERR_INVALID_ARG, "grid has %d tokens per frame, cache %d", grid.height * grid.width,
+                    c->tokens_per_frame);
+    if (grid.frames < 1 || grid.frames > c->capacity)
+        return fail(VDIT_ERR_INVALID_ARG, "frames %d must be in [1, capacity %d]", grid.frames, c->capacity);
+    if (t0 < 0 || (int64_t)t0 + grid.frames > INT32_MAX / 2) return fail(VDIT_ERR_INVALID_ARG, "t0 %d out of range", t0);
+    int32_t n = grid.frames * c->tokens_per_frame;
+    if ((st = check_tensor(k, "k", n, c->heads, c->head_dim))) return st;
+    if ((st = check_tensor(v, "v", n, c->heads, c->head_dim))) return st;
+    if (k.dtype != v.dtype) return fail(VDIT_ERR_INVALID_ARG, "k and v must have the same dtype");
+    *r = RopeDev{};
+    if (rope) {
+        if ((st = check_rope_use(rope, c->head_dim, grid, t0))) return st;
+        *r = rope_dev(rope);
+    }
+    return VDIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,28 +301,32 @@ int vdit_kv_cache_reset(vdit_kv_cache* c, void* stream) {
 
 int vdit_kv_append(vdit_kv_cache* c, const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0, vdit_tensor k,
                    vdit_tensor v, void* stream) {
-    int st = check_cache(c);
+    RopeDev r;
+    int st = check_append(c, rope, grid, t0, k, v, &r);
     if (st) return st;
-    if (!c->k || !c->v || !c->slot_frame_dev || !c->slot_frame_host)
-        return fail(VDIT_ERR_INVALID_ARG, "cache buffers must be set");
-    if ((st = check_grid(grid))) return st;
-    if (grid.height * grid.width != c->tokens_per_frame)
-        return fail(VDIT_ERR_INVALID_ARG, "grid has %d tokens per frame, cache %d", grid.height * grid.width,
-                    c->tokens_per_frame);
-    if (grid.frames < 1 || grid.frames > c->capacity)
-        return fail(VDIT_ERR_INVALID_ARG, "frames %d must be in [1, capacity %d]", grid.frames, c->capacity);
-    if (t0 < 0 || (int64_t)t0 + grid.frames > INT32_MAX / 2) return fail(VDIT_ERR_INVALID_ARG, "t0 %d out of range", t0);
-    int32_t n = grid.frames * c->tokens_per_frame;
-    if ((st = check_tensor(k, "k", n, c->heads, c->head_dim))) return st;
-    if ((st = check_tensor(v, "v", n, c->heads, c->head_dim))) return st;
-    if (k.dtype != v.dtype) return fail(VDIT_ERR_INVALID_ARG, "k and v must have the same dtype");
-    RopeDev r{};
-    if (rope) {
-        if ((st = check_rope_use(rope, c->head_dim, grid, t0))) return st;
-        r = rope_dev(rope);
-    }
     hipError_t e = launch_kv_append(*c, rope ? &r : nullptr, grid, t0, k, v, (hipStream_t)stream);
     if (e != hipSuccess) return device_status(e, "kv append kernel");
+    for (int32_t f = 0; f < grid.frames; ++f) c->slot_frame_host[(t0 + f) % c->capacity] = t0 + f;
+    return ok();
+}
+
+int vdit_kv_append_plan(vdit_kv_cache* c, const vdit_rope_cfg* rope, vdit_grid grid, int32_t t0, vdit_tensor k,
+                        vdit_tensor v, const vdit_mask_cfg* mask, int32_t* plan_dev, size_t cap_words,
+                        size_t* used_words, void* stream) {
+    RopeDev r;
+    int st = check_append(c, rope, grid, t0, k, v, &r);
+    if (st) return st;
+    if ((st = check_plan_args(mask, grid, t0, c))) return st;
+    if (!plan_dev) return fail(VDIT_ERR_INVALID_ARG, "plan_dev is NULL");
+    const PlanGeom g = make_geom(mask, grid, t0, c);
+    const int32_t nq = plan_qtile_count(g);
+    const size_t bound = plan_bound_words(nq, c->capacity);
+    if (cap_words < bound)
+        return fail(VDIT_ERR_BUFFER_TOO_SMALL, "device plan needs %zu words, have %zu", bound, cap_words);
+    if (used_words) *used_words = bound;
+    hipError_t e =
+        launch_kv_append_plan(*c, rope ? &r : nullptr, grid, t0, k, v, g, nq, plan_dev, (hipStream_t)stream);
+    if (e != hipSuccess) return device_status(e, "kv append + plan kernel");
     for (int32_t f = 0; f < grid.frames; ++f) c->slot_frame_host[(t0 + f) % c->capacity] = t0 + f;
     return ok();
 }

@@ -206,6 +206,11 @@ hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid 
                             vdit_tensor v, hipStream_t s);
 hipError_t launch_plan_build(const PlanGeom& g, const int32_t* slot_frame_dev, int32_t n_qtiles, int32_t* plan,
                              hipStream_t s);
+// The append and the device plan of the same chunk in one launch (two where the capacity
+// exceeds the plan workgroup's LDS slot table).
+hipError_t launch_kv_append_plan(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0,
+                                 vdit_tensor k, vdit_tensor v, const PlanGeom& g, int32_t n_qtiles, int32_t* plan,
+                                 hipStream_t s);
 
 struct AttnLaunch {
     vdit_tensor q, o;

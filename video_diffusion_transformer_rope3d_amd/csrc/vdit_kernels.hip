@@ -1,6 +1,8 @@
 // Bandwidth-bound kernels of libvdit: token positions, RoPE3D in place, the ring KV-cache
 // append (keys rotated at their global positions, values transposed) and the device
 // block-plan builder.
+#include <type_traits>
+
 #include "vdit_bf16.hpp"
 #include "vdit_internal.hpp"
 
@@ -71,32 +73,229 @@ __global__ void rope_inplace_kernel(RopeDev r, int32_t n, int32_t hw, int32_t wi
     store8<F32>(x, off, v);
 }
 
+// ---- device plan builder: one workgroup.
+// 1. Every tile's geometry (LDS) and its qtile words; the slot table into LDS, with the
+//    frames of an append of the same launch placed in their slots.
+// 2. One thread per (tile, slot) pair: the slot's within-frame key range for the tile,
+//    packed into LDS (the divisions of the visibility rule run in parallel here).
+// 3. Rounds of THREADS tiles, a thread per tile: it merges its slots' ranges into runs and
+//    counts them, a block scan turns the counts into row pointers, then it writes its spans.
+// Plans too large for the LDS tables take the same rounds with the ranges computed inline.
+// All integer, with the host builder's merge (plan_runs), so the words equal the host's.
+constexpr int kPlanMaxSlots = 1024;
+constexpr uint32_t kPlanNoRange = 0xFFFFFFFFu;
+
+template <int THREADS, int MAX_TILES, int PAIR_WORDS>
+struct PlanLds {
+    static constexpr int kThreads = THREADS, kMaxTiles = MAX_TILES, kPairWords = PAIR_WORDS;
+    int32_t slot[kPlanMaxSlots];
+    uint32_t range[PAIR_WORDS];  // (a | b << 16) of pair tile * capacity + slot
+    int32_t tq[MAX_TILES], piece[MAX_TILES];
+    int32_t wave_sum[THREADS / 64];
+    long long pairs[THREADS / 64];
+};
+
+// The standalone kernel: 1024 threads, tables for 2048 tiles and 16384 pairs (84 KB).
+using PlanLdsBig = PlanLds<1024, 2048, 16384>;
+// The plan workgroup of the append kernel: 256 threads, tables for 512 tiles and 6144
+// pairs (32 KB, shared with the append's transpose buffer).
+using PlanLdsAppend = PlanLds<256, 512, 6144>;
+
+// Frames [upd_t0, upd_t0 + upd_frames) are placed in slot t mod capacity before the plan
+// is built (upd_frames = 0: the slot table as it is); needs capacity <= kPlanMaxSlots.
+template <class L>
+__device__ void plan_build_block(const PlanGeom& g, const int32_t* slot_frame, int32_t upd_t0, int32_t upd_frames,
+                                 int32_t nq, int32_t* plan, L& lds) {
+    constexpr int T = L::kThreads, W = T / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t cap = g.capacity;
+    const bool slots_in_lds = cap <= kPlanMaxSlots;
+    const bool tables = slots_in_lds && nq <= L::kMaxTiles && (int64_t)nq * cap <= L::kPairWords && g.hw <= 0xFFFF;
+    int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
+    int32_t* row_ptr = qtiles + 2 * nq;
+    int32_t* spans = row_ptr + nq + 1;
+
+    for (int32_t i = tid; i < nq; i += T) {
+        const QTile qt = plan_qtile(g, i);
+        qtiles[2 * i] = qt.q_start;
+        qtiles[2 * i + 1] = qt.q_len;
+        if (tables) {
+            lds.tq[i] = qt.t_q;
+            lds.piece[i] = qt.piece;
+        }
+    }
+    if (slots_in_lds) {
+        for (int32_t j = tid; j < cap; j += T) {
+            // slot j after the append: the newest appended frame t with t mod cap = j, if any
+            int32_t t = slot_frame[j];
+            if (upd_frames > 0) {
+                const int32_t last = upd_t0 + upd_frames - 1;
+                const int32_t cand = last - ((last - j) % cap + cap) % cap;
+                if (cand >= upd_t0) t = cand;
+            }
+            lds.slot[j] = t;
+        }
+    }
+    __syncthreads();
+    const int32_t* sf = slots_in_lds ? lds.slot : slot_frame;
+    if (tables) {
+        for (int32_t p = tid; p < nq * cap; p += T) {
+            const int32_t i = p / cap, j = p - i * cap;
+            const QTile qt{0, 0, lds.tq[i], 0, lds.piece[i]};
+            int32_t a, b;
+            lds.range[p] = plan_slot_range(g, qt, sf[j], &a, &b) ? (uint32_t)a | ((uint32_t)b << 16) : kPlanNoRange;
+        }
+        __syncthreads();
+    }
+
+    // the spans of tile i, from the LDS table or computed inline
+    auto tile_runs = [&](int32_t i, const QTile& qt, auto&& emit) {
+        if (tables) {
+            const uint32_t* rr = lds.range + i * cap;
+            plan_runs(
+                cap, g.frame_stride,
+                [&](int32_t slot, int32_t* a, int32_t* b) {
+                    const uint32_t r = rr[slot];
+                    *a = (int32_t)(r & 0xFFFFu);
+                    *b = (int32_t)(r >> 16);
+                    return r != kPlanNoRange;
+                },
+                emit);
+        } else {
+            plan_tile_spans(g, sf, qt, emit);
+        }
+    };
+
+    int32_t carry = 0;
+    long long pairs = 0;
+    for (int32_t base = 0; base < nq; base += T) {
+        const int32_t i = base + tid;
+        int32_t cnt = 0;
+        QTile qt{0, 0, 0, 0, 0};
+        if (i < nq) {
+            qt = plan_qtile(g, i);
+            long long keys = 0;
+            tile_runs(i, qt, [&](int32_t, int32_t len) {
+                ++cnt;
+                keys += len;
+            });
+            pairs += keys * qt.q_len;
+        }
+        // block-wide inclusive scan of the counts: within the wave, then over the waves
+        int32_t incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        if (lane == 63) lds.wave_sum[wave] = incl;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+        for (int w = 0; w < W; ++w) {
+            const int32_t v = lds.wave_sum[w];
+            before += w < wave ? v : 0;
+            total += v;
+        }
+        __syncthreads();  // wave_sum is rewritten by the next round
+        incl += before;
+        if (i < nq) {
+            row_ptr[i + 1] = carry + incl;
+            int32_t kk = carry + incl - cnt;
+            tile_runs(i, qt, [&](int32_t st, int32_t len) {
+                spans[2 * kk] = st;
+                spans[2 * kk + 1] = len;
+                ++kk;
+            });
+        }
+        carry += total;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
+    if (lane == 0) lds.pairs[wave] = pairs;
+    __syncthreads();
+    if (tid == 0) {
+        long long tot_pairs = 0;
+        for (int w = 0; w < W; ++w) tot_pairs += lds.pairs[w];
+        const unsigned long long tot = (unsigned long long)tot_pairs;
+        row_ptr[0] = 0;
+        plan[0] = (int32_t)VDIT_PLAN_MAGIC;
+        plan[1] = VDIT_PLAN_VERSION;
+        plan[2] = g.kind;
+        plan[3] = g.tile;
+        plan[4] = nq;
+        plan[5] = carry;
+        plan[6] = (int32_t)(uint32_t)(tot & 0xFFFFFFFFull);
+        plan[7] = (int32_t)(uint32_t)(tot >> 32);
+    }
+}
+
+__global__ __launch_bounds__(PlanLdsBig::kThreads) void plan_build_kernel(PlanGeom g, const int32_t* slot_frame,
+                                                                          int32_t nq, int32_t* plan) {
+    __shared__ PlanLdsBig lds;
+    plan_build_block(g, slot_frame, 0, 0, nq, plan, lds);
+}
+
+// The plan built by the append kernel's extra workgroup: the call's own chunk as the query.
+struct AppendPlan {
+    PlanGeom g;
+    int32_t nq;
+    int32_t* plan;
+};
+
 // ---- KV append.  Block = 64 tokens x one head.  Every thread issues all its global loads
 // (K and V, then the RoPE (cos, sin) of its pairs) before its first store (the compiler
 // cannot move a load above a possibly aliasing store).  Keys: rotated (optional) and written
 // to k[h][phys][:].  Values: staged in LDS by token rows and written transposed to
 // v[h][d][phys], 16 bytes (8 consecutive keys of one channel row) per lane where the 8 keys
 // are consecutive in the ring (one frame, frames a multiple of 8 tokens), else key by key.
+// With PLAN, workgroup x = 0 of head 0 builds the plan of the same chunk (AppendPlan) from the
+// slot table with this append's frames placed, while the other workgroups append (token block
+// x - 1); the plan then costs no launch of its own and runs under the append.
 constexpr int kAppendTok = 64;
 
-template <int D, bool F32>
+template <int D>
+struct AppendLds {
+    static constexpr int PITCH = D + 2;  // bf16 elements per LDS row, odd dword count per row
+    uint16_t sv[kAppendTok * PITCH];
+};
+template <int D>
+union AppendPlanLds {
+    AppendLds<D> app;
+    PlanLdsAppend plan;
+};
+
+template <int D, bool F32, bool PLAN>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has_rope, int32_t n, int32_t hw,
                                                              int32_t width, int32_t t0, int32_t capacity,
                                                              int32_t frame_stride, int64_t kv_rows,
                                                              const void* k, int64_t k_st, int64_t k_sh,
                                                              const void* v, int64_t v_st, int64_t v_sh,
                                                              uint16_t* kc, uint16_t* vt, int32_t* slot_frame,
-                                                             int32_t frames) {
+                                                             int32_t frames, AppendPlan ap) {
     constexpr int CH = D / 8;
     constexpr int PER = kAppendTok * CH / kThreads;  // chunks per thread
-    constexpr int PITCH = D + 2;                     // bf16 elements per LDS row, odd dword count per row
+    constexpr int PITCH = AppendLds<D>::PITCH;
     constexpr int VT_ITEMS = D * (kAppendTok / 8) / kThreads;  // (channel, 8-key group) items per thread
-    __shared__ uint16_t sv[kAppendTok * PITCH];
+    __shared__ std::conditional_t<PLAN, AppendPlanLds<D>, AppendLds<D>> lds;
     const int32_t h = blockIdx.y;
-    const int32_t n0 = blockIdx.x * kAppendTok;
+    int32_t bx = blockIdx.x;
+    if constexpr (PLAN) {
+        if (bx == 0) {
+            if (h == 0) plan_build_block(ap.g, slot_frame, t0, frames, ap.nq, ap.plan, lds.plan);
+            return;
+        }
+        --bx;
+    }
+    uint16_t* sv;
+    if constexpr (PLAN)
+        sv = lds.app.sv;
+    else
+        sv = lds.sv;
+    const int32_t n0 = bx * kAppendTok;
     const int tid = threadIdx.x;
 
-    if (blockIdx.x == 0 && blockIdx.y == 0 && tid < frames) slot_frame[(t0 + tid) % capacity] = t0 + tid;
+    if (bx == 0 && h == 0)
+        for (int32_t f = tid; f < frames; f += kThreads) slot_frame[(t0 + f) % capacity] = t0 + f;
 
     float xk[PER][8], xv[PER][8];
 #pragma unroll
@@ -180,139 +379,6 @@ __global__ void kv_zero_pad_kernel(int32_t hw, int32_t frame_stride, int32_t t0,
     }
 }
 
-// ---- device plan builder: one workgroup of 1024 threads.
-// 1. Every tile's geometry (LDS) and its qtile words; the slot table into LDS.
-// 2. One thread per (tile, slot) pair: the slot's within-frame key range for the tile,
-//    packed into LDS (the divisions of the visibility rule run in parallel here).
-// 3. Rounds of 1024 tiles, a thread per tile: it merges its slots' ranges into runs and
-//    counts them, a block scan turns the counts into row pointers, then it writes its spans.
-// Plans too large for the LDS tables take the same rounds with the ranges computed inline.
-// All integer, with the host builder's merge (plan_runs), so the words equal the host's.
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPlanMaxSlots = 1024;
-constexpr int kPlanMaxTiles = 2048;
-constexpr int kPlanPairWords = 16384;
-constexpr uint32_t kPlanNoRange = 0xFFFFFFFFu;
-
-__global__ __launch_bounds__(kPlanThreads) void plan_build_kernel(PlanGeom g, const int32_t* slot_frame, int32_t nq,
-                                                                  int32_t* plan) {
-    __shared__ int32_t s_slot[kPlanMaxSlots];
-    __shared__ uint32_t s_range[kPlanPairWords];  // (a | b << 16) of pair tile * capacity + slot
-    __shared__ int32_t s_tq[kPlanMaxTiles], s_piece[kPlanMaxTiles];
-    __shared__ int32_t s_wave[kPlanWaves];
-    __shared__ long long s_pairs[kPlanWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t cap = g.capacity;
-    const bool tables = cap <= kPlanMaxSlots && nq <= kPlanMaxTiles && (int64_t)nq * cap <= kPlanPairWords &&
-                        g.hw <= 0xFFFF;
-    int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
-    int32_t* row_ptr = qtiles + 2 * nq;
-    int32_t* spans = row_ptr + nq + 1;
-
-    for (int32_t i = tid; i < nq; i += kPlanThreads) {
-        const QTile qt = plan_qtile(g, i);
-        qtiles[2 * i] = qt.q_start;
-        qtiles[2 * i + 1] = qt.q_len;
-        if (tables) {
-            s_tq[i] = qt.t_q;
-            s_piece[i] = qt.piece;
-        }
-    }
-    if (tables)
-        for (int32_t j = tid; j < cap; j += kPlanThreads) s_slot[j] = slot_frame[j];
-    __syncthreads();
-    if (tables) {
-        for (int32_t p = tid; p < nq * cap; p += kPlanThreads) {
-            const int32_t i = p / cap, j = p - i * cap;
-            const QTile qt{0, 0, s_tq[i], 0, s_piece[i]};
-            int32_t a, b;
-            s_range[p] = plan_slot_range(g, qt, s_slot[j], &a, &b) ? (uint32_t)a | ((uint32_t)b << 16) : kPlanNoRange;
-        }
-        __syncthreads();
-    }
-
-    // the spans of tile i, from the LDS table or computed inline
-    auto tile_runs = [&](int32_t i, const QTile& qt, auto&& emit) {
-        if (tables) {
-            const uint32_t* rr = s_range + i * cap;
-            plan_runs(
-                cap, g.frame_stride,
-                [&](int32_t slot, int32_t* a, int32_t* b) {
-                    const uint32_t r = rr[slot];
-                    *a = (int32_t)(r & 0xFFFFu);
-                    *b = (int32_t)(r >> 16);
-                    return r != kPlanNoRange;
-                },
-                emit);
-        } else {
-            plan_tile_spans(g, slot_frame, qt, emit);
-        }
-    };
-
-    int32_t carry = 0;
-    long long pairs = 0;
-    for (int32_t base = 0; base < nq; base += kPlanThreads) {
-        const int32_t i = base + tid;
-        int32_t cnt = 0;
-        QTile qt{0, 0, 0, 0, 0};
-        if (i < nq) {
-            qt = plan_qtile(g, i);
-            long long keys = 0;
-            tile_runs(i, qt, [&](int32_t, int32_t len) {
-                ++cnt;
-                keys += len;
-            });
-            pairs += keys * qt.q_len;
-        }
-        // block-wide inclusive scan of the counts: within the wave, then over the waves
-        int32_t incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-        }
-        if (lane == 63) s_wave[wave] = incl;
-        __syncthreads();
-        int32_t before = 0, total = 0;
-        for (int w = 0; w < kPlanWaves; ++w) {
-            const int32_t v = s_wave[w];
-            before += w < wave ? v : 0;
-            total += v;
-        }
-        __syncthreads();  // s_wave is rewritten by the next round
-        incl += before;
-        if (i < nq) {
-            row_ptr[i + 1] = carry + incl;
-            int32_t kk = carry + incl - cnt;
-            tile_runs(i, qt, [&](int32_t st, int32_t len) {
-                spans[2 * kk] = st;
-                spans[2 * kk + 1] = len;
-                ++kk;
-            });
-        }
-        carry += total;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) pairs += __shfl_xor(pairs, off);
-    if (lane == 0) s_pairs[wave] = pairs;
-    __syncthreads();
-    if (tid == 0) {
-        long long tot_pairs = 0;
-        for (int w = 0; w < kPlanWaves; ++w) tot_pairs += s_pairs[w];
-        const unsigned long long tot = (unsigned long long)tot_pairs;
-        row_ptr[0] = 0;
-        plan[0] = (int32_t)VDIT_PLAN_MAGIC;
-        plan[1] = VDIT_PLAN_VERSION;
-        plan[2] = g.kind;
-        plan[3] = g.tile;
-        plan[4] = nq;
-        plan[5] = carry;
-        plan[6] = (int32_t)(uint32_t)(tot & 0xFFFFFFFFull);
-        plan[7] = (int32_t)(uint32_t)(tot >> 32);
-    }
-}
-
 }  // namespace
 
 hipError_t launch_positions(vdit_grid grid, int32_t t0, int32_t* out, hipStream_t s) {
@@ -344,34 +410,58 @@ hipError_t launch_rope_inplace(const RopeDev& r, vdit_grid grid, int32_t t0, int
 
 template <int D, bool F32>
 static void append_d(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
-                     vdit_tensor v, hipStream_t s) {
+                     vdit_tensor v, const AppendPlan* ap, hipStream_t s) {
     int32_t hw = c.tokens_per_frame, n = grid.frames * hw;
     int32_t fs = frame_stride_of(hw);
     int64_t kv_rows = (int64_t)c.capacity * fs;
-    dim3 blocks((n + kAppendTok - 1) / kAppendTok, c.heads);
+    const unsigned token_blocks = (n + kAppendTok - 1) / kAppendTok;
     RopeDev rr = r ? *r : RopeDev{};
-    kv_append_kernel<D, F32><<<blocks, kThreads, 0, s>>>(
-        rr, r != nullptr, n, hw, grid.width, t0, c.capacity, fs, kv_rows, k.data, k.stride_token, k.stride_head,
-        v.data, v.stride_token, v.stride_head, static_cast<uint16_t*>(c.k), static_cast<uint16_t*>(c.v),
-        c.slot_frame_dev, grid.frames);
+    if (ap)
+        kv_append_kernel<D, F32, true><<<dim3(token_blocks + 1, c.heads), kThreads, 0, s>>>(
+            rr, r != nullptr, n, hw, grid.width, t0, c.capacity, fs, kv_rows, k.data, k.stride_token,
+            k.stride_head, v.data, v.stride_token, v.stride_head, static_cast<uint16_t*>(c.k),
+            static_cast<uint16_t*>(c.v), c.slot_frame_dev, grid.frames, *ap);
+    else
+        kv_append_kernel<D, F32, false><<<dim3(token_blocks, c.heads), kThreads, 0, s>>>(
+            rr, r != nullptr, n, hw, grid.width, t0, c.capacity, fs, kv_rows, k.data, k.stride_token,
+            k.stride_head, v.data, v.stride_token, v.stride_head, static_cast<uint16_t*>(c.k),
+            static_cast<uint16_t*>(c.v), c.slot_frame_dev, grid.frames, AppendPlan{});
     if (fs > hw)
         kv_zero_pad_kernel<D><<<dim3(grid.frames, c.heads), kThreads, 0, s>>>(
             hw, fs, t0, c.capacity, kv_rows, static_cast<uint16_t*>(c.k), static_cast<uint16_t*>(c.v));
 }
 
-hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
-                            vdit_tensor v, hipStream_t s) {
+static hipError_t kv_append_any(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0,
+                                vdit_tensor k, vdit_tensor v, const AppendPlan* ap, hipStream_t s) {
     // K and V share one kernel: both must have the same dtype
     if (k.dtype != v.dtype) return hipErrorInvalidValue;
     bool f32 = k.dtype == VDIT_DTYPE_FP32;
     if (c.head_dim == 128) {
-        if (f32) append_d<128, true>(c, r, grid, t0, k, v, s);
-        else append_d<128, false>(c, r, grid, t0, k, v, s);
+        if (f32) append_d<128, true>(c, r, grid, t0, k, v, ap, s);
+        else append_d<128, false>(c, r, grid, t0, k, v, ap, s);
     } else {
-        if (f32) append_d<64, true>(c, r, grid, t0, k, v, s);
-        else append_d<64, false>(c, r, grid, t0, k, v, s);
+        if (f32) append_d<64, true>(c, r, grid, t0, k, v, ap, s);
+        else append_d<64, false>(c, r, grid, t0, k, v, ap, s);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
+                            vdit_tensor v, hipStream_t s) {
+    return kv_append_any(c, r, grid, t0, k, v, nullptr, s);
+}
+
+hipError_t launch_kv_append_plan(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0,
+                                 vdit_tensor k, vdit_tensor v, const PlanGeom& g, int32_t n_qtiles, int32_t* plan,
+                                 hipStream_t s) {
+    if (c.capacity > kPlanMaxSlots) {  // the plan workgroup keeps the slot table in LDS: two launches
+        hipError_t e = kv_append_any(c, r, grid, t0, k, v, nullptr, s);
+        if (e != hipSuccess) return e;
+        plan_build_kernel<<<1, PlanLdsBig::kThreads, 0, s>>>(g, c.slot_frame_dev, n_qtiles, plan);
+        return hipGetLastError();
+    }
+    const AppendPlan ap{g, n_qtiles, plan};
+    return kv_append_any(c, r, grid, t0, k, v, &ap, s);
 }
 
 hipError_t launch_kv_zero_pad(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s) {
@@ -390,7 +480,7 @@ hipError_t launch_kv_zero_pad(const vdit_kv_cache& c, vdit_grid grid, int32_t t0
 
 hipError_t launch_plan_build(const PlanGeom& g, const int32_t* slot_frame_dev, int32_t n_qtiles, int32_t* plan,
                              hipStream_t s) {
-    plan_build_kernel<<<1, kPlanThreads, 0, s>>>(g, slot_frame_dev, n_qtiles, plan);
+    plan_build_kernel<<<1, PlanLdsBig::kThreads, 0, s>>>(g, slot_frame_dev, n_qtiles, plan);
     return hipGetLastError();
 }
 

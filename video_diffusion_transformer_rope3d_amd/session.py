@@ -34,6 +34,13 @@ class AttentionSession:
         frames = k.shape[0] // (self.frame_h * self.frame_w)
         B.vdit_kv_append(self.cache, self.rope if rotate else None, self.grid(frames), t0, k, v, self.stream)
 
+    def append_plan(self, k, v, t0, rotate=True, out=None):
+        """append(k, v, t0) and the device plan of the same frames as the query call, in one
+        launch."""
+        frames = k.shape[0] // (self.frame_h * self.frame_w)
+        return B.vdit_kv_append_plan(self.cache, self.rope if rotate else None, self.grid(frames), t0, k, v,
+                                     self.mask, out, self.stream)
+
     def plan(self, q_frames, q_t0, where=B.VDIT_WHERE_DEVICE, out=None):
         return B.vdit_plan_mask(self.mask, self.grid(q_frames), q_t0, self.cache, where, out, self.stream)
 
