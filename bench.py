@@ -12,10 +12,15 @@ region.
 --dynamic-tau builds the content-adaptive plan (pooled tile logits, adaptive threshold)
 in place of the static one; the step then carries the append and that plan's four launches.
 
-Prints one JSON line.  value = attention FLOP on computed blocks / step time (TFLOP/s);
-the attention kernel alone is timed with HIP events on its launch stream (mean and median
-over the timed steps, warm caches), and again over --cold-steps steps each preceded by a
-512 MiB scratch write that evicts the MALL and the L2s (cold: K/V, Q and plan from HBM).
+Before the W warmup steps, the step runs for 200 ms of wall time (clock_ramp_ms), so that the
+timed steps see the GPU at its sustained clocks.
+
+Prints one JSON line.  value = attention FLOP on computed blocks / step time (TFLOP/s), the
+step time taken over K steps back to back with HIP events only at the two ends; K more
+steps carry events around each launch, which time the attention kernel alone on its launch
+stream (mean and median, warm caches) and the append (+ plan) launch; --cold-steps more
+steps are each preceded by a 512 MiB scratch write that evicts the MALL and the L2s (cold:
+K/V, Q and plan from HBM).
 --library-reference adds the stock library call on the same shapes (torch's SDPA where every
 query sees every cached key; F.linear with --qkv) as context, timed the same way.
 """
@@ -115,22 +120,40 @@ def cpu_baseline(w, inputs, seconds):
                        f"({spent:.1f} s); the ring build (K rotation of all heads) is excluded")
 
 
+RAMP_SECONDS = 0.2
+
+
+def clock_ramp(fn, seconds=RAMP_SECONDS):
+    """Runs fn() in batches until `seconds` of wall time have passed: the GPU settles at its
+    sustained clocks only after tens of milliseconds of load, and the counted warmup steps of a
+    short call alone (a few milliseconds) would leave the timed steps on a rising clock."""
+    import torch
+    end = time.perf_counter() + seconds
+    while time.perf_counter() < end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_back_to_back(fn, steps, stream):
+    """ms per call of `steps` calls issued back to back, HIP events only at the two ends."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def time_library(fn, steps, warmup):
-    """Median ms of fn() over `steps` calls, HIP events on the current stream."""
+    """ms per call of a library call, timed as this library's calls are (back to back)."""
     import torch
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    times.sort()
-    return times[len(times) // 2]
+    return time_back_to_back(fn, steps, torch.cuda.current_stream())
 
 
 def library_attention(heads, n_q, n_k, head_dim, flop, steps, warmup):
@@ -205,16 +228,10 @@ def bench_rel_l1(args):
     cur = (prev.float() + 0.05 * torch.randn((nb, elems), device="cuda", generator=g)).to(torch.bfloat16)
     out = torch.empty(nb + 1, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    clock_ramp(lambda: B.vdit_block_rel_l1(cur, prev, out=out))
     for _ in range(args.warmup):
         B.vdit_block_rel_l1(cur, prev, out=out)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(stream)
-        B.vdit_block_rel_l1(cur, prev, out=out)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms = time_back_to_back(lambda: B.vdit_block_rel_l1(cur, prev, out=out), args.steps, stream)
     nbytes = 2 * nb * elems * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     cpu = None
@@ -231,7 +248,8 @@ def bench_rel_l1(args):
                "sample": f"one block ({tokens} x {hidden} elements, bf16 values in fp64), {reps} passes"}
     result = {
         "metric": "block reuse indicator: feature bytes read per second", "value": round(gbs, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "clock_ramp_ms": RAMP_SECONDS * 1e3,
+        "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "wan13b_block_features", "blocks": nb, "tokens": tokens, "hidden": hidden},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
@@ -262,16 +280,11 @@ def bench_qkv(args):
     q = torch.empty((n, heads, d), dtype=torch.bfloat16, device="cuda")
     grid = B.grid(frames, fh, fw)
     stream = torch.cuda.current_stream()
+    clock_ramp(lambda: B.vdit_qkv_rope_append(x, w, b, rope, grid, t0, cache, q_out=q))
     for _ in range(args.warmup):
         B.vdit_qkv_rope_append(x, w, b, rope, grid, t0, cache, q_out=q)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e0, e1 in ev:
-        e0.record(stream)
-        B.vdit_qkv_rope_append(x, w, b, rope, grid, t0, cache, q_out=q)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    ms = time_back_to_back(lambda: B.vdit_qkv_rope_append(x, w, b, rope, grid, t0, cache, q_out=q), args.steps,
+                           stream)
     flop = 2.0 * n * 3 * heads * d * hidden
     tf = flop / (ms * 1e-3) / 1e12
     cpu = None
@@ -291,7 +304,8 @@ def bench_qkv(args):
                "kind": "oracle", "sample": f"{rows} tokens of the chunk (one 1 x {rows} frame), {reps} passes"}
     result = {
         "metric": "fused QKV projection + RoPE + KV append TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "clock_ramp_ms": RAMP_SECONDS * 1e3,
+        "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "wan13b_chunk_qkv", "tokens": n, "hidden": hidden, "heads": heads, "head_dim": d},
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -386,6 +400,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    clock_ramp(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -393,16 +408,23 @@ def main():
     pairs = int(np.uint32(header[6])) + (int(np.uint32(header[7])) << 32)
     flop = 4.0 * w.head_dim * w.heads * pairs
 
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    # value: K steps back to back with events only at the two ends (an event between two
+    # launches costs a few microseconds of its own, which would be charged to the step)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    # per-launch times: K more steps with events around the append (+ plan) and the attention
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
     attn_times = [b.elapsed_time(c) for _, b, c in events]
     attn_avg = sum(attn_times) / args.steps
     prep_avg = sum(a.elapsed_time(b) for a, b, _ in events) / args.steps
@@ -429,6 +451,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_ms": RAMP_SECONDS * 1e3,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
