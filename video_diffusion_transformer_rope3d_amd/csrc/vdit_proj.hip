@@ -7,10 +7,11 @@
 // v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  With W as the A operand every lane owns
 // one token and holds the channels (r % 4) + 8 (r / 4) + 4 (lane / 32) of a 32-channel
 // block in its 16 accumulators, so the pairs (2i, 2i + 1) that RoPE rotates are in the same
-// lane.  A workgroup computes 128 features x 256 tokens (8 waves of 64 x 64); with
+// lane.  A workgroup computes 128 features x 128 tokens (4 waves of 64 x 64); with
 // head_dim 128 the features are one head of Q, K or V.  W and x tiles of 64 channels go from
-// global memory straight to LDS (buffer loads into LDS, XOR-swizzled rows) in a ring of three
-// stages, so the loads of the k-step two ahead are in flight while one is computed.
+// global memory straight to LDS (buffer loads into LDS, XOR-swizzled rows) in two stages, so
+// the loads of the next k-step are in flight while one is computed.  Two workgroups share a
+// CU (64 KB of LDS each), so one's epilogue and barrier waits overlap the other's MFMAs.
 // Epilogue: + bias, rotation of Q and K at (t0 + f, h, w) in fp32, one rounding to bf16;
 // Q to its output, K to the ring's K rows, V to the ring's transposed V rows.
 #include "vdit_bf16.hpp"
@@ -24,15 +25,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kPN = 128;                 // features per tile
-constexpr int kPM = 256;                 // tokens per tile
+constexpr int kPM = 128;                 // tokens per tile
 constexpr int kPK = 64;                  // hidden channels per k-step
-constexpr int kPWaves = 8;
+constexpr int kPWaves = 4;
 constexpr int kPThreads = kPWaves * 64;
 constexpr int kRowBytes = kPK * 2;       // 128 bytes per tile row
 constexpr int kWBytes = kPN * kRowBytes;  // 16 KB
-constexpr int kXBytes = kPM * kRowBytes;  // 32 KB
+constexpr int kXBytes = kPM * kRowBytes;  // 16 KB
 constexpr int kStage = kWBytes + kXBytes;
-constexpr int kNStage = 3;               // the k-step two ahead is in flight
+constexpr int kNStage = 2;               // the next k-step is in flight
 constexpr int kWLoads = kWBytes / 1024 / kPWaves, kXLoads = kXBytes / 1024 / kPWaves;  // per thread
 
 struct ProjArgs {
@@ -66,9 +67,9 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs; each XCD gets a contiguous range of
-// a tile list ordered in blocks of 4 token tiles x 8 feature tiles, so the ~32 workgroups an
-// XCD runs at once share 4 x tiles and 8 W tiles, which stay in its L2 (x and W of a chunk
-// are 14 MB each, more than one XCD's L2).
+// a tile list ordered in blocks of 8 token tiles x 8 feature tiles, so the 64 workgroups an
+// XCD runs at once (two per CU) share 8 x tiles and 8 W tiles, which stay in its L2 (x and W
+// of a chunk are 14 MB each, more than one XCD's L2).
 __device__ inline int xcd_item(int bid, int total) {
     constexpr int kXcd = 8;
     const int q = total / kXcd, r = total % kXcd, xcd = bid % kXcd, idx = bid / kXcd;
@@ -76,7 +77,7 @@ __device__ inline int xcd_item(int bid, int total) {
 }
 
 __device__ inline void block_tile(int item, int tok_tiles, int feat_tiles, int& tt, int& ft) {
-    constexpr int BT = 4, BF = 8;
+    constexpr int BT = 8, BF = 8;
     const int nbt = (tok_tiles + BT - 1) / BT, nbf = (feat_tiles + BF - 1) / BF;
     for (int bf = 0; bf < nbf; ++bf)
         for (int bt = 0; bt < nbt; ++bt) {
@@ -91,7 +92,7 @@ __device__ inline void block_tile(int item, int tok_tiles, int feat_tiles, int& 
     tt = ft = 0;  // not reached: item < tok_tiles * feat_tiles
 }
 
-__global__ __launch_bounds__(kPThreads, 1) void qkv_rope_append_kernel(ProjArgs a) {
+__global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kNStage * kStage];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
     if (blockIdx.x == 0)  // the device slot table, as the append kernel keeps it
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kPThreads, 1) void qkv_rope_append_kernel(ProjArgs 
     // fragments: row r of a tile, chunk c (8 channels) at r * 128 + ((c ^ swz(r)) * 16)
     const int sw = (li >> 1) & 7;
     const int wf_row = 64 * (wave & 1) + li;   // W rows of this wave (+ 32 fb)
-    const int xt_row = 64 * (wave >> 1) + li;  // x rows of this wave (+ 32 tb); wave >> 1 in 0..3
+    const int xt_row = 64 * (wave >> 1) + li;  // x rows of this wave (+ 32 tb); wave >> 1 in 0..1
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -177,21 +178,15 @@ __global__ __launch_bounds__(kPThreads, 1) void qkv_rope_append_kernel(ProjArgs 
     };
 
     const int nk = a.hidden / kPK;
-    static_assert(kWLoads + kXLoads == 6, "the waits below count one stage as 6 loads per thread");
     load_stage(0, smem);
-    if (nk > 1) {
-        load_stage(1, smem + kStage);
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // stage 0 landed
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     int st = 0;
     for (int kk = 0; kk < nk; ++kk) {
         char* cur = smem + st * kStage;
-        const int st2 = st == 0 ? 2 : st - 1;  // (kk + 2) mod 3
         if (kk == 0) load_epilogue_inputs();
-        if (kk + 2 < nk) load_stage(kk + 2, smem + st2 * kStage);
+        // the other stage was consumed before the last barrier
+        if (kk + 1 < nk) load_stage(kk + 1, smem + (st ^ 1) * kStage);
         // fragments of 16-channel step j + 1 are read while the MFMAs of step j run
         bf16x8 af[2][2], bf[2][2];
         auto read_frags = [&](int j, int b) {
@@ -220,15 +215,12 @@ __global__ __launch_bounds__(kPThreads, 1) void qkv_rope_append_kernel(ProjArgs 
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the next stage must have landed; the one after it may still be in flight.  A plain
-        // barrier: __syncthreads() would add a fence, which waits for every load in flight
-        // (vmcnt 0), the DMA of the stage two ahead included.  No fence is needed: each wave's
-        // own DMA is complete at its wait, and the fragment reads of this step were consumed
-        // by its MFMAs before the barrier.
-        if (kk + 2 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the next stage must have landed: each wave waits for its own DMA, then a plain
+        // barrier (no fence is needed: the fragment reads of this step were consumed by its
+        // MFMAs before the barrier).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
-        st = st == 2 ? 0 : st + 1;
+        st ^= 1;
     }
 
     // ---- epilogue.  The stages are free (the loop ended on a barrier).  Each wave turns its
