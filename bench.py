@@ -404,9 +404,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    header = plan[:8].cpu().numpy()
+    words = plan.cpu().numpy()
+    header = words[:8]
     pairs = int(np.uint32(header[6])) + (int(np.uint32(header[7])) << 32)
     flop = 4.0 * w.head_dim * w.heads * pairs
+    # work the kernels execute: every query tile as 128 rows (4 waves x 32), every span in whole
+    # 64-key tiles
+    nq = int(header[4])
+    row_ptr = words[8 + 2 * nq:8 + 3 * nq + 1]
+    spans = words[8 + 3 * nq + 1:8 + 3 * nq + 1 + 2 * int(header[5])].reshape(-1, 2)
+    padded_keys = sum(int(((spans[row_ptr[i]:row_ptr[i + 1], 1] + 63) // 64).sum()) * 64 for i in range(nq))
+    executed_flop = 4.0 * w.head_dim * w.heads * 128 * padded_keys
 
     # value: K steps back to back with events only at the two ends (an event between two
     # launches costs a few microseconds of its own, which would be charged to the step)
@@ -471,6 +479,7 @@ def main():
         "attn_ms_per_chunk_cold": round(float(np.median(cold)), 4) if cold else None,
         "attn_tflops": round(attn_tflops, 2),
         "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_valid_fraction": round(flop / executed_flop, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
