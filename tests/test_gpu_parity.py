@@ -132,6 +132,30 @@ def test_append_plan_equals_separate_calls(name):
     _assert_same_cache(a, b)
 
 
+@pytest.mark.parametrize("kind,fh,fw,cap,frames", [("dense", 64, 64, 21, 20), ("log_radial", 30, 52, 30, 30)],
+                         ids=["tiles_past_table", "pairs_past_table"])
+def test_append_plan_past_the_workgroup_tables(kind, fh, fw, cap, frames):
+    """Plans past the append launch's plan tables (more than 512 query tiles, more than 6144
+    (tile, slot) pairs): the plan workgroup computes the slot ranges inline."""
+    _print("append + plan past the tables", kind)
+    mk = lambda: AttentionSession(1, 64, fh, fw, cap, (24, 20, 20), 1e4, max_t=2 * cap + frames, mask=kind)
+    a, b = mk(), mk()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    hist = torch.randn((cap * fh * fw, 1, 64), device="cuda", generator=g).to(torch.bfloat16)
+    a.append(hist, hist, 0)
+    b.append(hist, hist, 0)
+    k = torch.randn((frames * fh * fw, 1, 64), device="cuda", generator=g).to(torch.bfloat16)
+    a.append(k, k, cap)
+    pa = a.plan(frames, cap)
+    pb = b.append_plan(k, k, cap)
+    torch.cuda.synchronize()
+    words = device_plan_words(pb)
+    assert int(words[4]) > 512 or int(words[4]) * cap > 6144
+    np.testing.assert_array_equal(words, device_plan_words(pa))
+    np.testing.assert_array_equal(words, b.plan(frames, cap, B.VDIT_WHERE_HOST))
+    _assert_same_cache(a, b)
+
+
 def test_append_plan_capacity_over_lds_table():
     """Capacity 1100 (beyond the plan workgroup's 1024-slot table): the two-launch path."""
     cap, fh, fw = 1100, 1, 8
