@@ -698,8 +698,40 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     // neighbouring workgroups, which share an XCD, work on neighbouring units with similar
     // key sets at the same time), then the units left over (fewer than G) as a stream:
     // their iterations laid end to end, every workgroup takes an equal contiguous share.
-    const int rounds = n_all / G;
-    const long long sk_base = (long long)(rounds * G / n_units) * t_head + u_pre[(rounds * G) % n_units];
+    // The stream balances the iterations exactly but splits units: a split costs a second
+    // segment start, a partial result written and read back, and keys read out of step with
+    // the neighbours.  So when the units do not fill whole rounds, the leftovers are taken as
+    // one more round of whole units instead (workgroups without a unit in it are idle) if the
+    // bound on a workgroup's work, the sum over rounds of the round's longest unit, exceeds
+    // the balanced share by at most 3/16 of it and by at most 40 iterations.
+    const int R = (n_all + G - 1) / G;
+    bool whole = false;
+    if (n_all % G != 0 && R <= 2 * T::STAGE / 4) {
+        int* s_rmax = reinterpret_cast<int*>(smem);  // [R], in the stages: free until the first segment
+        int& s_whole = *reinterpret_cast<int*>(tail + 108);
+        for (int r = tid; r < R; r += kThreads) s_rmax[r] = 0;
+        __syncthreads();
+        for (int j = tid; j < n_all; j += kThreads) {
+            const int k = j % n_units;
+            atomicMax(&s_rmax[j / G], u_pre[k + 1] - u_pre[k]);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            long long m = 0;
+            for (int r = lane; r < R; r += 64) m += s_rmax[r];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m += __shfl_xor(m, off);
+            if (lane == 0) {
+                const long long share = (total + G - 1) / G;
+                s_whole = m <= share + min(share * 3 / 16, 40LL);
+            }
+        }
+        __syncthreads();
+        whole = uniform(s_whole) != 0;
+    }
+    const int rounds = whole ? R : n_all / G;
+    const long long sk_base =
+        whole ? total : (long long)(rounds * G / n_units) * t_head + u_pre[(rounds * G) % n_units];
     const long long sk_len = total - sk_base;
     const long long B = sk_base + (long long)w * sk_len / G, E = sk_base + (long long)(w + 1) * sk_len / G;
 
@@ -760,8 +792,16 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
         long long ut;
         bool stream = true;
         if (phase == -1) {
-            const int j = round * G + w;
-            h = j / n_units, k = j % n_units, ut = 0, ib = 0, ie = -1, slot = 0;
+            int j = round * G + w;
+            if (whole && round == rounds - 1) {
+                // the last round's L units in equal contiguous shares per XCD (the idle workgroups
+                // spread over all XCDs); j = n_all: no unit
+                constexpr int kXcd = 8;
+                const int L = n_all - round * G, q = L / kXcd, r = L % kXcd;
+                const int xcd = blockIdx.x % kXcd, idx = blockIdx.x / kXcd;
+                j = idx < q + (xcd < r ? 1 : 0) ? round * G + xcd * q + min(xcd, r) + idx : n_all;
+            }
+            h = j / n_units, k = j % n_units, ut = 0, ib = 0, ie = j < n_all ? -1 : 0, slot = 0;
             stream = false;
             if (++round == rounds) phase = sk_phase;
         } else if (phase == 0) {
