@@ -4,15 +4,17 @@
 // double-buffered in LDS, the next tile's global loads are in flight while the current
 // tile is computed.  Keys outside the spans are never loaded.
 //
-// Work distribution (stream-K): the grid is persistent, as many workgroups as fit on the
-// device at once.  The key iterations of all (head, query tile) pairs are laid end to end
-// and every workgroup takes an equal contiguous share, so no CU idles while others finish
-// a last partial wave of tiles.  A tile whose iterations are split over several
-// workgroups is finished by the one that arrives last: the others leave their unnormalised
-// partial O^T with its running max and sum in a workspace and count themselves in on a
-// per-tile counter; the last one merges all partials in iteration order (deterministic)
-// and writes O and the LSE.  No workgroup ever waits on another, so the schedule needs no
-// co-residency guarantee.
+// Work distribution of the unit kernel: the grid is persistent, as many workgroups as fit on
+// the device at once.  Units (pairs of query tiles with equal span lists) go out in rounds
+// of whole units; the units that do not fill a last round either run as one more round of
+// whole units (when that costs a workgroup little more than the balanced share) or have
+// their key iterations laid end to end, every workgroup taking an equal contiguous share
+// (stream-K), so no CU idles while others finish a last partial wave.  A unit whose
+// iterations are split over several workgroups is finished by the one that arrives last:
+// the others leave their unnormalised partial O^T with its running max and sum in a
+// workspace and count themselves in on a per-unit counter; the last one merges all partials
+// in a fixed order (deterministic) and writes O and the LSE.  No workgroup ever waits on
+// another, so the schedule needs no co-residency guarantee.
 //
 // Math per key tile (FlashAttention-style online softmax, exact up to rounding): the
 // scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so every
