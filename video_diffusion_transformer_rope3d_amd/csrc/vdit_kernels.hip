@@ -102,9 +102,11 @@ using PlanLdsBig = PlanLds<1024, 2048, 16384>;
 using PlanLdsAppend = PlanLds<256, 512, 6144>;
 
 // Frames [upd_t0, upd_t0 + upd_frames) are placed in slot t mod capacity before the plan
-// is built (upd_frames = 0: the slot table as it is); needs capacity <= kPlanMaxSlots.
+// is built (upd_frames = 0: the slot table as it is); needs capacity <= kPlanMaxSlots.  With
+// an update, this workgroup is also the only writer of the device table: each thread writes
+// back the slots it changed after reading them.
 template <class L>
-__device__ void plan_build_block(const PlanGeom& g, const int32_t* slot_frame, int32_t upd_t0, int32_t upd_frames,
+__device__ void plan_build_block(const PlanGeom& g, int32_t* slot_frame, int32_t upd_t0, int32_t upd_frames,
                                  int32_t nq, int32_t* plan, L& lds) {
     constexpr int T = L::kThreads, W = T / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -131,7 +133,10 @@ __device__ void plan_build_block(const PlanGeom& g, const int32_t* slot_frame, i
             if (upd_frames > 0) {
                 const int32_t last = upd_t0 + upd_frames - 1;
                 const int32_t cand = last - ((last - j) % cap + cap) % cap;
-                if (cand >= upd_t0) t = cand;
+                if (cand >= upd_t0) {
+                    t = cand;
+                    slot_frame[j] = t;
+                }
             }
             lds.slot[j] = t;
         }
@@ -232,7 +237,8 @@ __device__ void plan_build_block(const PlanGeom& g, const int32_t* slot_frame, i
 __global__ __launch_bounds__(PlanLdsBig::kThreads) void plan_build_kernel(PlanGeom g, const int32_t* slot_frame,
                                                                           int32_t nq, int32_t* plan) {
     __shared__ PlanLdsBig lds;
-    plan_build_block(g, slot_frame, 0, 0, nq, plan, lds);
+    // no update: the table is only read
+    plan_build_block(g, const_cast<int32_t*>(slot_frame), 0, 0, nq, plan, lds);
 }
 
 // The plan built by the append kernel's extra workgroup: the call's own chunk as the query.
@@ -249,8 +255,9 @@ struct AppendPlan {
 // v[h][d][phys], 16 bytes (8 consecutive keys of one channel row) per lane where the 8 keys
 // are consecutive in the ring (one frame, frames a multiple of 8 tokens), else key by key.
 // With PLAN, workgroup x = 0 of head 0 builds the plan of the same chunk (AppendPlan) from the
-// slot table with this append's frames placed, while the other workgroups append (token block
-// x - 1); the plan then costs no launch of its own and runs under the append.
+// slot table with this append's frames placed, and writes those slots of the device table,
+// while the other workgroups append (token block x - 1); the plan then costs no launch of its
+// own and runs under the append.
 constexpr int kAppendTok = 64;
 
 template <int D>
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
     const int32_t n0 = bx * kAppendTok;
     const int tid = threadIdx.x;
 
-    if (bx == 0 && h == 0)
+    if (!PLAN && bx == 0 && h == 0)  // with PLAN the plan workgroup updates the table
         for (int32_t f = tid; f < frames; f += kThreads) slot_frame[(t0 + f) % capacity] = t0 + f;
 
     float xk[PER][8], xv[PER][8];
