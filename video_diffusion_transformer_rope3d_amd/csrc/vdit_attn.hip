@@ -161,6 +161,8 @@ __device__ inline void load_tile_lds(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_
     }
 }
 
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Logical workgroup index.  Workgroups are dispatched round-robin over the 8 XCDs; the
@@ -461,6 +463,12 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
     if (sp_begin < sp_end) {
         int span = sp_begin;
         int k0 = plan_word(spans + 2 * span), kend = k0 + plan_word(spans + 2 * span + 1);
+        // The words of the span after the current one, loaded when the current one starts with a
+        // vector load (counted by vmcnt, so the tile waits cover it), so that crossing into the
+        // next span does not wait for a plan read before the next tile's DMA is issued.
+        const __amdgpu_buffer_rsrc_t rsp = head_rsrc(spans, (uint32_t)sp_end * 8);
+        u32x2 pf = {0u, 0u};
+        if (span + 1 < sp_end) pf = __builtin_amdgcn_raw_buffer_load_b64(rsp, (uint32_t)(span + 1) * 8, 0, 0);
         const int wave_u = uniform(wave);
         const DmaLane<D / 8> kdl = dma_lane<D / 8>(wave_u, lane);
         const DmaLane<kBN / 8> vdl = dma_lane<kBN / 8>(wave_u, lane);
@@ -481,8 +489,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
             if (nk0 >= kend) {
                 ++nspan;
                 if (nspan < sp_end) {
-                    nk0 = plan_word(spans + 2 * nspan);
-                    nkend = nk0 + plan_word(spans + 2 * nspan + 1);
+                    nk0 = uniform((int)pf[0]);
+                    nkend = nk0 + uniform((int)pf[1]);
+                    if (nspan + 1 < sp_end)
+                        pf = __builtin_amdgcn_raw_buffer_load_b64(rsp, (uint32_t)(nspan + 1) * 8, 0, 0);
                 }
             }
             const bool has_next = nspan < sp_end;
@@ -545,7 +555,6 @@ __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(const int32_t
 
 // ---------------------------------------------------------------- unit kernel
 constexpr int kSc1 = 16;  // cache-policy operand of the buffer builtins: device scope (sc1)
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Floats of one workgroup's partial result: per wave the O^T accumulators of its 64 lanes
 // (DB * 16 floats each, stored float4-interleaved over lanes) and the lanes' (max, sum).
