@@ -450,8 +450,11 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
     const int r_in = wave * 32 + qi;
     const bool row_valid = r_in < q_len;
     const int row = q_start + (row_valid ? r_in : q_len - 1);
+    // a wave whose 32 rows all lie past the tile's end (the short last tile of a frame) keeps
+    // its share of the DMA and the barriers but skips the math
+    const bool wave_rows = uniform(wave) * 32 < q_len;
     bf16x8 qreg[KS];
-    load_q_rows<D, QF32>(a, h, row, g, qreg);
+    if (wave_rows) load_q_rows<D, QF32>(a, h, row, g, qreg);
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -499,7 +502,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
             if (has_next)
                 load_tile_lds<D, kTileWaves>(rk, rv, vpitch, nk0, nkend, wave_u, kdl, vdl,
                                              smem + (buf ^ 1) * T::STAGE);
-            tile_step<D, kTileWaves>(smem + buf * T::STAGE, fl, qreg, oacc, m_run, l_run, c, lazy_raw, k0, kend);
+            if (wave_rows)
+                tile_step<D, kTileWaves>(smem + buf * T::STAGE, fl, qreg, oacc, m_run, l_run, c, lazy_raw, k0, kend);
             if (!has_next) break;
             wait_tile_loads();
             __syncthreads();
@@ -841,9 +845,11 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
         if (ie > ib) {
             // ---- this wave's query tile of the unit (the second tile may not exist)
             const int my_tile = grp == 0 ? q : (unit_partner(k) ? q + 1 : -1);
-            const bool active = my_tile >= 0;  // uniform per wave
-            const int q_start = active ? plan_word(qtiles + 2 * my_tile) : 0;
-            const int q_len = active ? plan_word(qtiles + 2 * my_tile + 1) : 1;
+            const int q_start = my_tile >= 0 ? plan_word(qtiles + 2 * my_tile) : 0;
+            const int q_len = my_tile >= 0 ? plan_word(qtiles + 2 * my_tile + 1) : 1;
+            // uniform per wave: the tile exists and holds some of the wave's 32 rows (a wave past
+            // the end of a short tile keeps its share of the DMA and the barriers, nothing else)
+            const bool active = my_tile >= 0 && uniform(wave % kTileWaves) * 32 < q_len;
             const int r_in = (wave % kTileWaves) * 32 + qi;
             const bool row_valid = active && r_in < q_len;
             const int row = q_start + (r_in < q_len ? r_in : q_len - 1);
