@@ -10,8 +10,9 @@ Readings where the page is silent:
   pieces of each cached frame (the last piece of a frame is ragged);
 * proxy: the mean of the pre-softmax logits scale * <q_rot, k_rot> over all query-key
   pairs of a (query tile, key tile), summed over heads so that one plan serves every head.
-  By linearity it equals scale * sum_h <mean of the tile's q_rot, mean of the tile's k_rot>,
-  which is how `proxies` computes it (the pins compute the mean of the logit block itself);
+  `proxies` computes exactly that: the logit block of each tile pair, then its mean (the
+  pins check it against the factorised form scale * sum_h <mean q_rot, mean k_rot>, which
+  linearity makes equal, and against a hand-built case);
 * candidates: the key tiles the static rule of the call lets the query tile see;
 * adaptive threshold: per query tile, with M and m the largest and smallest candidate
   proxies, a candidate with proxy p is kept when p - m >= (1 - tau) * (M - m), tau in
@@ -47,12 +48,21 @@ def key_tiles(k_phys, k_t, k_s, tile: int):
 
 
 def proxies(q, q_pos, k_rot, qtiles, ktiles, dims, theta, scale):
-    """P[i, j] = scale * sum_h <mean q_rot over query tile i, mean k_rot over key tile j>."""
+    """P[i, j] = mean over the query rows of tile i and the keys of tile j of the logit
+    scale * sum_h <q_rot, k_rot>: the logits of each query tile against every key are formed
+    head by head, then each key tile's block of them is averaged."""
     q_rot = rope3d(np.asarray(q, dtype=np.float64), q_pos, dims, theta)  # [Nq, H, D]
     k_rot = np.asarray(k_rot, dtype=np.float64)
-    qbar = np.stack([q_rot[q0:q0 + ql].mean(axis=0) for q0, ql in qtiles])  # [nq, H, D]
-    kbar = np.stack([k_rot[idx].mean(axis=0) for idx in ktiles])  # [nk, H, D]
-    return scale * np.einsum("ihd,jhd->ij", qbar, kbar)
+    heads = q_rot.shape[1]
+    p = np.zeros((len(qtiles), len(ktiles)))
+    for i, (q0, ql) in enumerate(qtiles):
+        logits = np.zeros((ql, k_rot.shape[0]))
+        for h in range(heads):
+            logits += q_rot[q0:q0 + ql, h, :] @ k_rot[:, h, :].T
+        logits *= scale
+        for j, idx in enumerate(ktiles):
+            p[i, j] = logits[:, idx].mean()
+    return p
 
 
 def candidates(mask, q_t, q_s, qtiles, ktiles, k_t, k_s):

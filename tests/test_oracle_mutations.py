@@ -107,8 +107,10 @@ MUTATIONS = [
     ("masks.py", "        acc += len(sp)\n        words.append(acc)", "        words.append(acc)\n        acc += len(sp)",
      "row pointers shifted by one tile"),
     # dynamic-threshold plan
-    ("dynamic.py", "qbar = np.stack([q_rot[q0:q0 + ql].mean(axis=0) for q0, ql in qtiles])",
-     "qbar = np.stack([q_rot[q0:q0 + ql].sum(axis=0) for q0, ql in qtiles])", "query tile summed, not averaged"),
+    ("dynamic.py", "p[i, j] = logits[:, idx].mean()", "p[i, j] = logits[:, idx].sum() / len(idx)",
+     "logit block summed over the query rows, not averaged"),
+    ("dynamic.py", "logits += q_rot[q0:q0 + ql, h, :] @ k_rot[:, h, :].T",
+     "logits += q_rot[q0:q0 + ql, h, :] @ k_rot[:, 0, :].T", "every head scored against head 0's keys"),
     ("dynamic.py", "(p - small[:, None]) >= (1.0 - tau) * (big - small)[:, None]",
      "(p - small[:, None]) >= tau * (big - small)[:, None]", "threshold fraction inverted"),
     ("dynamic.py", "c[i, j] = vis.all()", "c[i, j] = True", "candidates ignore the static rule"),
