@@ -288,7 +288,11 @@ def test_zero_queries_average_visible_values(name):
         np.testing.assert_allclose(o[row], want, atol=2e-3, rtol=1e-2, err_msg=f"row {row}")
 
 
-def test_fused_rope_equals_standalone_rope():
+def test_fused_rope_and_standalone_rope_both_match_the_oracle():
+    """Q rotated while the attention kernel loads it, or rotated beforehand by vdit_rope3d_qk and
+    passed with rope = NULL: both match the oracle.  The kernel folds the softmax scale into Q
+    before rounding it to bf16, so the fused path rounds Q once and the standalone path twice (its
+    rotated bf16 Q, then the scaled one): the two agree to the usual bar, not bit for bit."""
     w = get_workload("small_chunk_pad")
     inp = make_inputs(w)
     fused = run_workload(w, inp)
@@ -297,7 +301,13 @@ def test_fused_rope_equals_standalone_rope():
     s = fused["session"]
     o2 = s.attend(qd, w.q_frames, w.q_t0, fused["plan"], rotate=False)
     torch.cuda.synchronize()
-    assert torch.equal(o2, fused["o"])
+    st = oracle.build_state(w, inp)
+    a, b = fused["o"].float().cpu().numpy(), o2.float().cpu().numpy()
+    for h in range(w.heads):
+        ref, _ = oracle.attention_rows(st, h)
+        compare(a[:, h], ref, what=f"fused rope, head {h}")
+        compare(b[:, h], ref, what=f"standalone rope, head {h}")
+        compare(b[:, h], a[:, h], what=f"standalone vs fused, head {h}")
 
 
 def test_chunk_by_chunk_equals_whole_call():

@@ -74,6 +74,9 @@ __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lazy-rescale margin of the pipelined loop (log2 units): p = exp2(s - m) < 2^kLazyP.
+constexpr float kLazyP = 8.0f;
+
 // swap bits 2 and 3
 __device__ inline int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -195,8 +198,11 @@ __device__ inline int plan_word(const int32_t* p) {
 // All row loads are issued first, then the table loads of half the chunks at a time (a
 // bound on live registers), so the segment start waits for a few round trips instead of
 // one per chunk.
+// qscale multiplies the rotated row before its one bf16 rounding (the unit kernel folds the
+// softmax scale and log2(e) into Q, so its scores come out in log2 units).
 template <int D, bool QF32>
-__device__ __forceinline__ void load_q_rows(const AttnArgs& a, int h, int row, int g, bf16x8 (&qreg)[D / 16]) {
+__device__ __forceinline__ void load_q_rows(const AttnArgs& a, int h, int row, int g, bf16x8 (&qreg)[D / 16],
+                                            float qscale = 1.0f) {
     constexpr int KS = D / 16, HALF = KS / 2;
     using Raw = std::conditional_t<QF32, float4, u32x4>;
     constexpr int PER = QF32 ? 2 : 1;  // 16-byte loads per chunk of 8 channels
@@ -246,6 +252,8 @@ __device__ __forceinline__ void load_q_rows(const AttnArgs& a, int h, int row, i
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rope_apply(cs[i][e], x[2 * e], x[2 * e + 1]);
             }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= qscale;
             qreg[ks] = __builtin_bit_cast(bf16x8, pack_bf16x8(x));
         }
     }
@@ -557,6 +565,251 @@ __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(const int32_t
     }
 }
 
+// ---------------------------------------------------------------- pipelined key loop
+// The unit kernel's key loop is software-pipelined inside each wave: while the softmax of key
+// tile n runs on the VALU, the score MFMAs of tile n + 1 run on the matrix core, then the
+// P.V MFMAs of tile n follow, interleaved with the row sum of tile n and the row max of tile
+// n + 1.  A step therefore reads K of tile n + 1 and V^T of tile n, while the DMA of tile
+// n + 2 is in flight: three LDS stages.  The K tiles of the three stages come first, then
+// the V^T tiles, so every fragment read takes its stage and block as an immediate offset.
+template <int D>
+struct Pipe {
+    static constexpr int KS = D / 16;  // k-steps of the score contraction
+    static constexpr int DB = D / 32;  // 32-row blocks of O^T
+    static constexpr int KCH = D / 8, VCH = kBN / 8;
+    static constexpr int KROW = KCH * 16, VROW = VCH * 16;  // LDS bytes per K row / V^T row
+    static constexpr int K_BYTES = kBN * KROW, V_BYTES = D * VROW;
+    static constexpr int V_BASE = 3 * K_BYTES;
+    static constexpr int BYTES = 3 * (K_BYTES + V_BYTES);
+    static constexpr int NS = 2 * KS;   // score MFMAs per step
+    static constexpr int NP = 4 * DB;   // P.V MFMAs per step
+    static constexpr int NM = NS + NP;
+    static constexpr int LOOK = 2;      // fragment reads issued this many MFMAs ahead
+};
+
+// Per-lane LDS byte offsets of the fragment reads in stage 0: the K fragment of k-step ks
+// (key block 0; block 1 is 32 rows further) and the V^T fragment of 16-key group j (row block
+// 0; block db is 32 V^T rows further).  Rows hold 16-byte chunks at position chunk ^ swz(row)
+// (see Tile), which the DMA writes.
+template <int D>
+struct PipeLane {
+    uint32_t k[D / 16];
+    uint32_t v[4];
+};
+
+template <int D>
+__device__ inline PipeLane<D> pipe_lane(int qi, int g) {
+    using P = Pipe<D>;
+    PipeLane<D> pl;
+    const int krow = swap23(qi);
+    const int kswz = swz<P::KCH>(krow), vswz = swz<P::VCH>(qi);
+#pragma unroll
+    for (int ks = 0; ks < P::KS; ++ks) pl.k[ks] = (uint32_t)(krow * P::KROW + (((2 * ks + g) ^ kswz) * 16));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pl.v[j] = (uint32_t)(P::V_BASE + qi * P::VROW + (((2 * j + g) ^ vswz) * 16));
+    // the offsets are lane constants of the whole segment loop; kept opaque so that the
+    // compiler does not rematerialise them inside the loop
+#pragma unroll
+    for (int ks = 0; ks < P::KS; ++ks) asm volatile("" : "+v"(pl.k[ks]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(pl.v[j]));
+    return pl;
+}
+
+// DMA of key tile [k0, k0 + kBN) of a span ending at kend into K stage / V^T stage `st`.
+template <int D, int WAVES>
+__device__ inline void pipe_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t vpitch, int k0,
+                                 int kend, int wave, const DmaLane<D / 8>& kl, const DmaLane<kBN / 8>& vl, char* smem,
+                                 int st) {
+    using T = Tile<D, WAVES>;
+    using P = Pipe<D>;
+    constexpr int KRPB = 64 / T::KCH, VRPB = 64 / T::VCH;
+    char* kdst = smem + st * P::K_BYTES;
+    char* vdst = smem + P::V_BASE + st * P::V_BYTES;
+    const int last = kend - 1 - k0;
+#pragma unroll
+    for (int i = 0; i < T::K_LOADS; ++i) {
+        const int blk = i * WAVES + wave;
+        const int rowd = min(blk * KRPB + kl.rib, last);
+        const uint32_t voff = (uint32_t)rowd * (D * 2) + kl.chunk * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, voff,
+                                                 (uint32_t)k0 * (D * 2), 0, 0);
+    }
+    const int vkey = min(k0 + vl.chunk * 8, (kend - 1) & ~7);
+    const uint32_t vcol = (uint32_t)(vkey - k0) * 2;
+#pragma unroll
+    for (int i = 0; i < T::V_LOADS; ++i) {
+        const int blk = i * WAVES + wave;
+        const uint32_t voff = (uint32_t)vl.rib * vpitch + vcol;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, voff,
+                                                 (uint32_t)(blk * VRPB) * vpitch + (uint32_t)k0 * 2, 0, 0);
+    }
+}
+
+// Masks the keys >= lim of a score tile (lim = valid keys of the tile minus 8 g): S row
+// kb * 32 + (r >> 3) * 16 + (r & 7) + 8 g of the lane's accumulator element r.
+__device__ inline void pipe_mask(f32x16 (&s)[2], int lim) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (kb * 32 + (r >> 3) * 16 + (r & 7) >= lim) s[kb][r] = -INFINITY;
+}
+
+// Row max of a score tile: this lane's 32 keys, then the other half of the row (lane ^ 32)
+// through a VALU lane swap.
+__device__ inline float pipe_row_max(const f32x16 (&s)[2]) {
+    float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int t = 1; t < 16; ++t) mt = fmaxf(fmaxf(mt, s[t >> 3][2 * (t & 7)]), s[t >> 3][2 * (t & 7) + 1]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// End of a step (rare, uniform branch): the next tile is the ragged end of a span (mask its
+// scores and take its max again) or its max exceeds the exponent base by more than the lazy
+// margin (raise the base by mt; O, the row sum, the new scores and negm follow).  Scores are
+// relative to the base and in log2 units, so p = exp2(s) stays below 2^kLazy.
+template <int D>
+__device__ __forceinline__ void pipe_fixup(f32x16 (&sn)[2], bool tail, int lim, float mt, float& m_run,
+                                           float& l_run, f32x16 (&oacc)[D / 32], f32x16& negm) {
+    if (tail) {
+        pipe_mask(sn, lim);
+        mt = pipe_row_max(sn);
+    }
+    if (__any(mt > kLazyP)) {
+        const float d = fmaxf(mt, 0.f);  // the base rises by d >= 0
+        const float alpha = fast_exp2(-d);
+        m_run += d;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sn[kb] -= d;
+        negm = f32x16{} - m_run;
+    }
+}
+
+// First tile of a segment: its row max becomes the exponent base (the ragged end of a span
+// masked first), the scores are taken relative to it and negm holds -base.
+__device__ inline void pipe_first(f32x16 (&s)[2], bool tail, int lim, float& m_run, f32x16& negm) {
+    if (tail) pipe_mask(s, lim);
+    const float mt = pipe_row_max(s);
+    m_run = mt;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] -= mt;
+    negm = f32x16{} - mt;
+}
+
+// Score MFMAs of one tile, not interleaved (the segment's first tile): S^T = K Q^T from K stage st.
+template <int D>
+__device__ __forceinline__ void pipe_scores(const char* smem, const PipeLane<D>& pl, int st,
+                                            const bf16x8 (&qreg)[D / 16], f32x16 (&sn)[2]) {
+    using P = Pipe<D>;
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < P::KS; ++ks)
+            sn[kb] = mfma32(*reinterpret_cast<const bf16x8*>(smem + pl.k[ks] + st * P::K_BYTES + kb * 32 * P::KROW),
+                            qreg[ks], sn[kb]);
+}
+
+// One step of the pipelined loop.  Scores are in log2 units (Q carries the softmax scale
+// and log2(e)), and their accumulators start from negm (every element -m, m the exponent
+// base), so the MFMAs give s - m and the exponentials take them as they are.
+// In: s = S^T - m of tile n (masked), V^T of tile n in stage ST, K of tile n + 1 in stage ST1.
+// Out: sn = S^T - m of tile n + 1 (unmasked), mt_next = its row max; O^T and the row sum
+// include tile n.
+//
+// Four quarters, each a run of MFMAs with VALU work spread evenly between them:
+//   1. scores of key block 0 of tile n + 1   | exponentials and bf16 packing of key group 0,
+//                                               half of group 1
+//   2. P.V of key groups 0, 1 of tile n      | the rest of group 1 (done before the first
+//                                               group-1 MFMA), group 2
+//   3. scores of key block 1 of tile n + 1   | group 3, max of the new key block 0
+//   4. P.V of key groups 2, 3 of tile n      | max of the new key block 1 and of the row's
+//                                               other half, row sum of the packed P
+// About 20 VALU items per quarter: with the VALU work piled into the first half of the step
+// (its dependency order) both waves of a SIMD saturate the VALU there while the matrix core
+// waits.  Groups 0, 1 of tile n are the scores of its key block 0, which quarter 1 consumes
+// while it builds block 0 of tile n + 1; so at most three 16-register score blocks are live.
+// Each MFMA with its share of VALU work and its fragment read LOOK MFMAs ahead is one
+// scheduling group, in this order.
+template <int D, int ST, int ST1>
+__device__ __forceinline__ void pipe_step(const char* smem, const PipeLane<D>& pl, const bf16x8 (&qreg)[D / 16],
+                                          f32x16 (&oacc)[D / 32], const f32x16 (&s)[2], f32x16 (&sn)[2],
+                                          const f32x16& negm, float& l_run, float& mt_next) {
+    using P = Pipe<D>;
+    constexpr int KS = P::KS, DB = P::DB, NM = P::NM, L = P::LOOK;
+    constexpr int Q1 = KS, Q2 = Q1 + 2 * DB, Q3 = Q2 + KS;  // quarter boundaries
+    auto is_score = [](int i) { return i < Q1 || (i >= Q2 && i < Q3); };
+    auto score_ks = [](int i) { return i < Q1 ? i : i - Q2; };
+    auto score_kb = [](int i) { return i < Q1 ? 0 : 1; };
+    auto pv_index = [](int i) { return i < Q2 ? i - Q1 : i - Q3 + 2 * DB; };  // 0 .. NP-1
+    // fragment of MFMA i
+    auto frag = [&](int i) -> bf16x8 {
+        if (is_score(i))
+            return *reinterpret_cast<const bf16x8*>(smem + pl.k[score_ks(i)] + ST1 * P::K_BYTES +
+                                                    score_kb(i) * 32 * P::KROW);
+        const int pi = pv_index(i), j = pi / DB, db = pi % DB;
+        return *reinterpret_cast<const bf16x8*>(smem + pl.v[j] + ST * P::V_BYTES + db * 32 * P::VROW);
+    };
+    float x[32];
+    uint32_t pw[16];
+    float mt = 0.f;
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    // VALU item k of quarter q.  Softmax items are numbered 12 j + u over key groups j (u < 8:
+    // exponential, else a bf16 pack); quarters 1, 2 and the first 12 items of quarter 3 take
+    // them in order, then come the row max and the row sum.
+    auto valu = [&](int q, int k) {
+        const int gidx = q == 0 ? k : q == 1 ? 18 + k : q == 2 && k < 12 ? 36 + k : -1;
+        if (gidx >= 0) {
+            const int jj = gidx / 12, u = gidx % 12;
+            const int base = jj * 8;
+            if (u < 8) x[base + u] = fast_exp2(s[jj >> 1][(jj & 1) * 8 + u]);
+            else pw[jj * 4 + u - 8] = pack_bf16x2(x[base + 2 * (u - 8)], x[base + 2 * (u - 8) + 1]);
+        } else if (q == 2) {  // max of the new key block 0
+            const int t = k - 12;
+            if (t == 0) mt = fmaxf(sn[0][0], sn[0][1]);
+            else mt = fmaxf(fmaxf(mt, sn[0][2 * t]), sn[0][2 * t + 1]);
+        } else if (k < 8) {  // max of the new key block 1
+            mt = fmaxf(fmaxf(mt, sn[1][2 * k]), sn[1][2 * k + 1]);
+        } else if (k == 8) {  // and of the other half of the row (lane ^ 32)
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        } else {  // row sum of the bf16-rounded P (the weights P.V uses), two per dot product
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[k - 9]), one2, l_run, false);
+        }
+    };
+    bf16x8 fr[L + 1];
+#pragma unroll
+    for (int i = 0; i < L; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        if (i + L < NM) fr[(i + L) % (L + 1)] = frag(i + L);
+        const bf16x8 a = fr[i % (L + 1)];
+        if (is_score(i)) {
+            const int kb = score_kb(i), ks = score_ks(i);
+            sn[kb] = mfma32(a, qreg[ks], ks == 0 ? negm : sn[kb]);
+        } else {
+            const int pi = pv_index(i), j = pi / DB, db = pi % DB;
+            const u32x4 pj = {pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]};
+            oacc[db] = mfma32(a, __builtin_bit_cast(bf16x8, pj), oacc[db]);
+        }
+        const int q = i < Q1 ? 0 : i < Q2 ? 1 : i < Q3 ? 2 : 3;
+        const int q0 = q == 0 ? 0 : q == 1 ? Q1 : q == 2 ? Q2 : Q3;
+        const int n = (q == 0 ? Q1 : q == 1 ? Q2 : q == 2 ? Q3 : NM) - q0, r = i - q0;
+        const int items = q < 2 ? 18 : q == 2 ? 20 : 25;
+        const int k_lo = items * r / n, k_hi = items * (r + 1) / n;
+#pragma unroll
+        for (int k = k_lo; k < k_hi; ++k) valu(q, k);
+        sched_fence();
+    }
+    mt_next = mt;
+}
+
 // ---------------------------------------------------------------- unit kernel
 constexpr int kSc1 = 16;  // cache-policy operand of the buffer builtins: device scope (sc1)
 
@@ -580,13 +833,14 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     // One LDS object only (with several, the compiler can no longer tell the tile DMA's LDS
     // writes from the fragment reads and waits for every DMA before reading a stage): the
     // two tile stages, the unit table and a few words of schedule state.
-    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE + kTableBytes + 256];
-    static_assert(5 * kMaxTiles <= 2 * T::STAGE, "per-tile scratch of the table build must fit the stages");
-    int* u_tile = reinterpret_cast<int*>(smem + 2 * T::STAGE);  // [units]: first tile | partner << 30
+    using PP = Pipe<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[PP::BYTES + kTableBytes + 256];
+    static_assert(5 * kMaxTiles <= PP::BYTES, "per-tile scratch of the table build must fit the stages");
+    int* u_tile = reinterpret_cast<int*>(smem + PP::BYTES);  // [units]: first tile | partner << 30
     int* u_pre = u_tile + kMaxTiles + 1;                        // [units + 1]: prefix of unit iterations
     int* t_it = reinterpret_cast<int*>(smem);                   // per-tile scratch in the stages
     unsigned char* t_same = reinterpret_cast<unsigned char*>(smem + 4 * kMaxTiles);
-    char* tail = smem + 2 * T::STAGE + kTableBytes;
+    char* tail = smem + PP::BYTES + kTableBytes;
     int* s_pos = reinterpret_cast<int*>(tail + 64);   // [4]
     int& s_arrived = *reinterpret_cast<int*>(tail + 96);
     int& s_bad = *reinterpret_cast<int*>(tail + 100);
@@ -721,7 +975,7 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     // the balanced share by at most 3/16 of it and by at most 40 iterations.
     const int R = (n_all + G - 1) / G;
     bool whole = false;
-    if (n_all % G != 0 && R <= 2 * T::STAGE / 4) {
+    if (n_all % G != 0 && R <= PP::BYTES / 4) {
         int* s_rmax = reinterpret_cast<int*>(smem);  // [R], in the stages: free until the first segment
         int& s_whole = *reinterpret_cast<int*>(tail + 108);
         for (int r = tid; r < R; r += kThreads) s_rmax[r] = 0;
@@ -779,16 +1033,14 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     };
 
     const float c = a.scale_log2;
-    const float lazy_raw = kLazy / c;
+    // the exponent base m_run and the merge below are in log2 units (Q carries c)
     const __amdgpu_buffer_rsrc_t rpart = head_rsrc(a.part, (uint32_t)((size_t)2 * G * P::SLOT * 4));
     const int wave_u = uniform(wave);
     const DmaLane<D / 8> kdl = dma_lane<D / 8>(wave_u, lane);
     const DmaLane<kBN / 8> vdl = dma_lane<kBN / 8>(wave_u, lane);
     const uint32_t head_bytes = (uint32_t)(a.kv_rows * D * 2);
     const uint32_t vpitch = (uint32_t)(a.kv_rows * 2);
-    FragLane fl;
-    fl.qi = qi, fl.g = g, fl.krow = swap23(qi);
-    fl.kswz = swz<T::KCH>(fl.krow), fl.vswz = swz<T::VCH>(qi);
+    const PipeLane<D> pl = pipe_lane<D>(qi, g);
 
     // Segment order of the stream share.  The unit l segment (from its first iteration) comes
     // first, then the whole units, each started at the iteration index equal to the stream
@@ -875,42 +1127,74 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
             int k0 = span_k0 + skip * kBN, kend = span_k0 + plan_word(spans + 2 * span + 1);
             const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.kc + (int64_t)h * a.kv_rows * D, head_bytes);
             const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.vt + (int64_t)h * D * a.kv_rows, head_bytes);
+            // Key tiles of the segment: n (k0, kend), n + 1 (k1, kend1), and the span of the
+            // furthest tile located so far.  A span ends in a ragged tile; whole units wrap
+            // from the last span to the first.
+            int left = ie - ib - 1;  // tiles after tile n
+            int k1 = 0, kend1 = 0;
+            auto advance = [&](int k, int ke, int& nk, int& nke) {
+                nk = k + kBN;
+                nke = ke;
+                if (nk >= ke) {
+                    span = span + 1 == sp_end ? sp_begin : span + 1;
+                    nk = plan_word(spans + 2 * span);
+                    nke = nk + plan_word(spans + 2 * span + 1);
+                }
+            };
             __syncthreads();  // the previous segment's LDS reads are done
-            load_tile_lds<D, kUnitWaves>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem);
-            // Q loads overlap the first K/V tile
-            if (active) load_q_rows<D, QF32>(a, h, row, g, qreg);
-
+            pipe_load<D, kUnitWaves>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem, 0);
+            if (left >= 1) {
+                advance(k0, kend, k1, kend1);
+                pipe_load<D, kUnitWaves>(rk, rv, vpitch, k1, kend1, wave_u, kdl, vdl, smem, 1);
+            }
+            // Q loads overlap the first K/V tiles; Q carries the softmax scale and log2(e)
+            if (active) load_q_rows<D, QF32>(a, h, row, g, qreg, c);
             wait_tile_loads();
             __syncthreads();
-            // The loop is unrolled by the two stages, so that each stage's LDS address is a
-            // constant (the fragment reads take it as their immediate offset instead of
-            // adding it per read).
-            int left = ie - ib - 1;
-            auto key_step = [&](auto bufc) {  // returns false after the segment's last tile
-                constexpr int BUF = decltype(bufc)::value;
-                int nk0 = k0 + kBN, nkend = kend;
-                if (left > 0 && nk0 >= kend) {
-                    span = span + 1 == sp_end ? sp_begin : span + 1;
-                    nk0 = plan_word(spans + 2 * span);
-                    nkend = nk0 + plan_word(spans + 2 * span + 1);
-                }
-                if (left > 0)
-                    load_tile_lds<D, kUnitWaves>(rk, rv, vpitch, nk0, nkend, wave_u, kdl, vdl, smem + (BUF ^ 1) * T::STAGE);
-                if (active)
-                    tile_step<D, kUnitWaves>(smem + BUF * T::STAGE, fl, qreg, oacc, m_run, l_run, c, lazy_raw, k0, kend);
-                if (left == 0) return false;
+            f32x16 sacc[2][2];
+            f32x16 negm;
+            if (active) {
+                pipe_scores<D>(smem, pl, 0, qreg, sacc[0]);
+                pipe_first(sacc[0], k0 + kBN > kend, kend - k0 - g * 8, m_run, negm);
+            }
+            // Step n: tile n's V^T is in stage n mod 3 and tile n + 1's K in the next stage; the
+            // loop is unrolled by 6 (three stages times two score buffers) so that stages and
+            // buffers are constants.
+            auto key_step = [&](auto stc, auto sbc) {  // returns false after the segment's last tile
+                constexpr int ST = decltype(stc)::value, SB = decltype(sbc)::value;
+                constexpr int ST1 = (ST + 1) % 3, ST2 = (ST + 2) % 3;
+                // tile n + 1 has landed (every wave's share of its DMA) and stage ST2 is free:
+                // every wave is done with tile n - 1
                 wait_tile_loads();
                 __syncthreads();
+                int k2 = 0, kend2 = 0;
+                if (left >= 2) {
+                    advance(k1, kend1, k2, kend2);
+                    pipe_load<D, kUnitWaves>(rk, rv, vpitch, k2, kend2, wave_u, kdl, vdl, smem, ST2);
+                }
+                if (active) {
+                    float mt;
+                    pipe_step<D, ST, ST1>(smem, pl, qreg, oacc, sacc[SB], sacc[SB ^ 1], negm, l_run, mt);
+                    if (left >= 1)
+                        pipe_fixup<D>(sacc[SB ^ 1], k1 + kBN > kend1, kend1 - k1 - g * 8, mt, m_run, l_run, oacc, negm);
+                }
+                if (left == 0) return false;
                 --left;
-                k0 = nk0;
-                kend = nkend;
+                k0 = k1;
+                kend = kend1;
+                k1 = k2;
+                kend1 = kend2;
                 return true;
             };
-            while (key_step(std::integral_constant<int, 0>{}) && key_step(std::integral_constant<int, 1>{})) {
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            while (key_step(I0{}, I0{}) && key_step(I1{}, I1{}) && key_step(I2{}, I0{}) && key_step(I0{}, I1{}) &&
+                   key_step(I1{}, I0{}) && key_step(I2{}, I1{})) {
             }
 
             if (ib == 0 && ie == n) {
-                if (active) store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, c);
+                if (active) store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, 1.0f);
             } else {
                 // Split unit: leave the partial in this workgroup's slot (0: the first unit of
                 // its share, 1: the last), then count in.  Partials are written and read with
@@ -926,7 +1210,9 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                             const u32x4 v = {__float_as_uint(oacc[db][4 * j]), __float_as_uint(oacc[db][4 * j + 1]),
                                              __float_as_uint(oacc[db][4 * j + 2]),
                                              __float_as_uint(oacc[db][4 * j + 3])};
-                            __builtin_amdgcn_raw_buffer_store_b128(v, rpart, pw + ((db * 4 + j) * 64 + lane) * 16, 0,
+                            // the block's constant offset goes to the scalar offset, so the lane
+                            // needs one address register for all sixteen stores
+                            __builtin_amdgcn_raw_buffer_store_b128(v, rpart, pw + lane * 16, (db * 4 + j) * 1024,
                                                                    kSc1);
                         }
                     const u32x2 ml = {__float_as_uint(m_run), __float_as_uint(l_run)};
@@ -946,18 +1232,13 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (active) {
                         // Segments are folded in descending share order, the same order
-                        // whichever workgroup merges.  The last arriver usually holds the last
-                        // segment; its partial is then the first one folded, which leaves it
-                        // unchanged, so it is taken from the registers instead of being re-read.
-                        int ulast = u1;
-                        while (wg_begin(ulast + 1) == wg_begin(ulast)) --ulast;
-                        const bool own_first = ulast == w;
-                        float M = own_first ? m_run : -INFINITY, L = own_first ? l_run : 0.f;
-                        if (!own_first) {
+                        // whichever workgroup merges, all of them from the workspace (this
+                        // workgroup's own partial too: O and its row state start empty here, so
+                        // the accumulators of the key loop are free).
+                        float M = -INFINITY, L = 0.f;
 #pragma unroll
-                            for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-                        }
-                        for (int u = own_first ? ulast - 1 : ulast; u >= u0; --u) {
+                        for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+                        for (int u = u1; u >= u0; --u) {
                             const long long ub = wg_begin(u);
                             if (wg_begin(u + 1) == ub) continue;
                             const uint32_t pu = (uint32_t)(((2 * u + (ub >= ut ? 0 : 1)) * P::SLOT + wave * P::WAVE) * 4);
@@ -965,22 +1246,25 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                                 __builtin_amdgcn_raw_buffer_load_b64(rpart, pu + P::O_FLOATS * 4 + lane * 8, 0, kSc1);
                             const float mu = __uint_as_float(mlu[0]), lu = __uint_as_float(mlu[1]);
                             const float mn = fmaxf(M, mu);
-                            const float a1 = M == -INFINITY ? 0.f : fast_exp2((M - mn) * c);
-                            const float a2 = mu == -INFINITY ? 0.f : fast_exp2((mu - mn) * c);
+                            const float a1 = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+                            const float a2 = mu == -INFINITY ? 0.f : fast_exp2(mu - mn);
+                            // one 32-row block at a time (a bound on the loads in flight)
 #pragma unroll
-                            for (int db = 0; db < DB; ++db)
+                            for (int db = 0; db < DB; ++db) {
 #pragma unroll
                                 for (int j = 0; j < 4; ++j) {
                                     const u32x4 vu = __builtin_amdgcn_raw_buffer_load_b128(
-                                        rpart, pu + ((db * 4 + j) * 64 + lane) * 16, 0, kSc1);
+                                        rpart, pu + lane * 16, (db * 4 + j) * 1024, kSc1);
 #pragma unroll
                                     for (int e = 0; e < 4; ++e)
                                         oacc[db][4 * j + e] = oacc[db][4 * j + e] * a1 + __uint_as_float(vu[e]) * a2;
                                 }
+                                sched_fence();
+                            }
                             L = L * a1 + lu * a2;
                             M = mn;
                         }
-                        store_rows<D, OF32>(a, h, row, row_valid, g, oacc, M, L, c);
+                        store_rows<D, OF32>(a, h, row, row_valid, g, oacc, M, L, 1.0f);
                     }
                 }
             }
