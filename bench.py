@@ -227,11 +227,13 @@ def bench_rel_l1(args):
     prev = torch.randn((nb, elems), device="cuda", generator=g).to(torch.bfloat16)
     cur = (prev.float() + 0.05 * torch.randn((nb, elems), device="cuda", generator=g)).to(torch.bfloat16)
     out = torch.empty(nb + 1, dtype=torch.float32, device="cuda")
+    ws = B.Workspace()
+    ws.get(B.vdit_block_rel_l1_workspace_bytes(nb, elems))  # allocated before the timed calls
     stream = torch.cuda.current_stream()
-    clock_ramp(lambda: B.vdit_block_rel_l1(cur, prev, out=out))
+    clock_ramp(lambda: B.vdit_block_rel_l1(cur, prev, out=out, workspace=ws))
     for _ in range(args.warmup):
-        B.vdit_block_rel_l1(cur, prev, out=out)
-    ms = time_back_to_back(lambda: B.vdit_block_rel_l1(cur, prev, out=out), args.steps, stream)
+        B.vdit_block_rel_l1(cur, prev, out=out, workspace=ws)
+    ms = time_back_to_back(lambda: B.vdit_block_rel_l1(cur, prev, out=out, workspace=ws), args.steps, stream)
     nbytes = 2 * nb * elems * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     cpu = None

@@ -13,15 +13,14 @@
  *   touched.  vdit_last_error() returns a message for the calling thread's last error.
  *   Faults inside a kernel surface at the caller's next synchronisation; a launch the
  *   runtime rejects returns VDIT_ERR_DEVICE.
- * - Memory: every buffer passed in is allocated and owned by the caller.  Pointers
- *   documented "device" must be device memory of the current HIP device, "host" plain
- *   host memory.  Three calls keep a scratch workspace of their own per (device, stream),
- *   allocated on first need and kept until the process ends, each documented at the call:
- *   vdit_block_attn_fwd (split-unit partials and counters), vdit_plan_dynamic (pooled
- *   tiles and proxies) and vdit_block_rel_l1 (per-chunk partial sums).  Besides those
- *   and the per-thread error string the library keeps no global state.
+ * - Memory: every buffer passed in is allocated and owned by the caller, the scratch
+ *   workspaces of vdit_block_attn_fwd, vdit_plan_dynamic and vdit_block_rel_l1 included
+ *   (each has a *_workspace_bytes size query).  Pointers documented "device" must be device
+ *   memory of the current HIP device, "host" plain host memory.  The library allocates no
+ *   memory and keeps no global state besides a per-thread error string.
  * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
- *   work is only enqueued; no call synchronises the device.
+ *   work is only enqueued; no call synchronises the device or a stream.  Calls that may run
+ *   at the same time must not share a workspace.
  * - Tensors [tokens][heads][channels]: vdit_tensor gives the base pointer, dtype and the
  *   token / head strides in ELEMENTS; channels are contiguous.  Base pointers must be
  *   16-byte aligned and strides multiples of 8 (bf16) or 4 (fp32) elements.
@@ -37,7 +36,7 @@
 extern "C" {
 #endif
 
-#define VDIT_ABI_VERSION 1
+#define VDIT_ABI_VERSION 2
 
 /* status codes */
 #define VDIT_OK 0
@@ -240,19 +239,23 @@ int vdit_kv_append_plan(vdit_kv_cache* cache, const vdit_rope_cfg* rope, vdit_gr
  * q, rope: as for vdit_block_attn_fwd (the proxies use fp32 rotated queries).
  * plan_dev: device, cap_words >= vdit_plan_dynamic_bound.  proxies_dev: NULL or device fp32
  * [n_qtiles][capacity * ceil(tokens_per_frame / tile)] (written; empty slots give 0).
- * Memory: a workspace per (device, stream) for the pooled tiles and proxies, allocated on the
- * first call that needs more (hipMalloc) and kept until the process ends.
+ * workspace: device scratch of at least vdit_plan_dynamic_workspace_bytes(base, q_grid, q_t0,
+ *   cache) bytes (pooled queries and keys, partial proxies, run counts), fully rewritten by
+ *   every call; its contents need no initialisation.
  * Errors: as vdit_plan_mask and vdit_block_attn_fwd; tau outside [0, 1] -> INVALID_ARG;
- *   more than 4096 key tiles (capacity * ceil(tokens_per_frame / tile)) -> UNSUPPORTED. */
+ *   more than 4096 key tiles (capacity * ceil(tokens_per_frame / tile)) -> UNSUPPORTED;
+ *   workspace NULL or below the size query -> BUFFER_TOO_SMALL. */
 typedef struct {
     float tau;
     float softmax_scale; /* scale of the proxy logits; <= 0 selects 1/sqrt(head_dim) */
 } vdit_dynamic_cfg;
 int vdit_plan_dynamic_bound(const vdit_mask_cfg* base, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
                             size_t* max_words);
+int vdit_plan_dynamic_workspace_bytes(const vdit_mask_cfg* base, vdit_grid q_grid, int32_t q_t0,
+                                      const vdit_kv_cache* cache, size_t* bytes);
 int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vdit_tensor q, const vdit_rope_cfg* rope,
                       vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache, int32_t* plan_dev, size_t cap_words,
-                      float* proxies_dev, void* stream);
+                      float* proxies_dev, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- attention forward: the full spatiotemporal softmax attention of "DynamicRad ..."
  * section 1 and "Accelerating Video Generation Inference ..." section 1, restricted to
@@ -269,21 +272,27 @@ int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vd
  *   natural-log log-sum-exp of each row's scaled logits (-inf for a row with no visible
  *   key, whose output is 0).
  * Arithmetic: bf16 products with fp32 accumulation, fp32 online softmax, P rounded to
- * bf16 before the P.V product.  A query tile's keys may be split over several workgroups,
- * whose partial results are merged in a fixed order: outputs are deterministic for a given
- * device.
- * Memory: the library keeps a workspace per (device, stream), allocated (hipMalloc, with a
- * device synchronisation) on the first call that needs more and kept until the process ends.
- * For CHUNK_CAUSAL and DENSE static plans it holds per-tile counters (4 bytes per head and
- * query tile) and partial results (two 135 KB slots per CU for head_dim 128); for dynamic
- * plans, the order of the query tiles (4 bytes per tile; tiles with more keys run first).  Calls on one stream are ordered;
- * calls that may run at the same time must use different streams.
+ * bf16 before the P.V product; the softmax scale (times log2 e) is applied to Q before its
+ * bf16 rounding.  A query tile's keys may be split over several workgroups, whose partial
+ * results are merged in a fixed order: outputs are deterministic for a given device.
+ * workspace: device scratch of at least vdit_block_attn_workspace_bytes(mask, q_grid, q_t0,
+ *   cache) bytes, asked on the device that runs the call (the size depends on its CU count;
+ *   0 for static log-radial plans, which need none).  For CHUNK_CAUSAL and DENSE plans it
+ *   holds per-tile arrival counters (4 bytes per head and query tile), which must be zero
+ *   before the workspace's first use and which every call leaves zero, and partial results
+ *   (two 135 KB slots per CU); for dynamic plans, the order of the query tiles.  The caller
+ *   zeroes a new workspace once (all bytes) and may pass it to any later call on the same
+ *   device whose size query does not exceed its size; every region sits at an offset that
+ *   depends on the device only.  Calls that may run at the same time need separate workspaces.
  * Errors: head counts or head_dim differing from the cache's, head_dim not 64 or 128 ->
  * INVALID_ARG / UNSUPPORTED; more than 4096 query tiles in one call -> UNSUPPORTED (split the
- * call by frames); allocation failure -> DEVICE. */
+ * call by frames); workspace NULL or below the size query -> BUFFER_TOO_SMALL. */
+int vdit_block_attn_workspace_bytes(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0,
+                                    const vdit_kv_cache* cache, size_t* bytes);
 int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
                         const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
-                        float softmax_scale, vdit_tensor o, float* lse, void* stream);
+                        float softmax_scale, vdit_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ---- fused QKV projection + RoPE3D + K/V append ("Accelerating Video Generation Inference ...",
  * section 2.C, the QKV projection and the rotary embedding as one kernel with precomputed
@@ -320,12 +329,14 @@ int vdit_qkv_rope_append(vdit_tensor x, int32_t hidden, const void* w_qkv, int64
  * out_dev: device fp32 [n_blocks + 1]: r_0 .. r_{n_blocks-1}, then the mean.
  * Arithmetic: fp32 sums over chunks of 32768 elements, chunk sums added in fp64 in chunk
  *   order (deterministic).
- * Memory: a workspace per (device, stream) for the chunk sums (8 bytes per chunk and block),
- *   allocated (hipMalloc) on the first call that needs more and kept until the process ends.
+ * workspace: device scratch of at least vdit_block_rel_l1_workspace_bytes(n_blocks,
+ *   block_elems) bytes (8 per chunk and block), fully rewritten by every call.
  * Errors: NULL pointers, n_blocks outside [1, 65535], block_elems < 0, bad stride or alignment
- *   -> INVALID_ARG; other dtypes -> UNSUPPORTED. */
+ *   -> INVALID_ARG; other dtypes -> UNSUPPORTED; workspace NULL or below the size query ->
+ *   BUFFER_TOO_SMALL. */
+int vdit_block_rel_l1_workspace_bytes(int32_t n_blocks, int64_t block_elems, size_t* bytes);
 int vdit_block_rel_l1(const void* cur, const void* prev, int32_t dtype, int32_t n_blocks, int64_t block_elems,
-                      int64_t block_stride, float* out_dev, void* stream);
+                      int64_t block_stride, float* out_dev, void* workspace, size_t workspace_bytes, void* stream);
 
 /* vdit_reuse_decide (host only): the reuse flags of every block at diffusion step `step`
  * (0-based, < total_steps) given the latest indicator (the mean from vdit_block_rel_l1).

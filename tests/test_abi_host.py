@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol(L):
     assert declared == set(B.EXPORTS), declared ^ set(B.EXPORTS)
     for name in declared:
         assert hasattr(L, name)
-    assert B.vdit_abi_version() == 1
+    assert B.vdit_abi_version() == 2
     assert B.vdit_status_string(2) == "buffer too small"
 
 
@@ -242,19 +242,70 @@ def test_attention_errors(L):
     t = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 128, 64)
     g = B.grid(3, 4, 6)
     # null plan, null output, grid mismatch, bad scale is fine (defaults) but head mismatch is not
-    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(m), None, 0.0, t, None,
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(m), None, 0.0, t, None, None, 0,
                                  None) == B.VDIT_ERR_INVALID_ARG
     assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0,
-                                 B.VditTensor(None, 0, 0, 128, 64), None, None) == B.VDIT_ERR_INVALID_ARG
+                                 B.VditTensor(None, 0, 0, 128, 64), None, None, 0, None) == B.VDIT_ERR_INVALID_ARG
     assert L.vdit_block_attn_fwd(t, None, B.grid(3, 4, 5), 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
-                                 None, None) == B.VDIT_ERR_INVALID_ARG
+                                 None, None, 0, None) == B.VDIT_ERR_INVALID_ARG
     narrow = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 64, 32)  # head stride below head_dim
     assert L.vdit_block_attn_fwd(narrow, None, g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t, None,
-                                 None) == B.VDIT_ERR_INVALID_ARG
+                                 None, 0, None) == B.VDIT_ERR_INVALID_ARG
     rope = B.rope_cfg(128, (44, 42, 42), 1e4, 16, 4, 6)  # head_dim differs from the cache's
     rope.table = fake
     assert L.vdit_block_attn_fwd(t, ctypes.byref(rope), g, 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
-                                 None, None) == B.VDIT_ERR_INVALID_ARG
+                                 None, None, 0, None) == B.VDIT_ERR_INVALID_ARG
+
+
+def test_workspace_size_queries_and_short_workspaces(L):
+    """The calls that need scratch memory take it from the caller: their size queries are host
+    arithmetic (the attention call's unit-kernel plans also ask the device's CU count, which a
+    host without a GPU cannot answer), and a missing or short workspace is refused before any
+    launch."""
+    slots = np.array([0, 1, 2], np.int32)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    desc = B.VditKVCache(fake, fake, fake, slots.ctypes.data, 3, 24, 2, 64)
+    g = B.grid(3, 4, 6)
+    t = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    n = ctypes.c_size_t(123)
+    # static log-radial plans run one tile per workgroup and need no workspace
+    radial = B.mask_cfg("log_radial")
+    assert L.vdit_block_attn_workspace_bytes(ctypes.byref(radial), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # dynamic plans: the order of the query tiles (4096 words)
+    dyn_m = B.dynamic_mask(B.mask_cfg("chunk_causal", 1))
+    assert L.vdit_block_attn_workspace_bytes(ctypes.byref(dyn_m), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
+    assert n.value == 4096 * 4
+    assert L.vdit_block_attn_workspace_bytes(ctypes.byref(dyn_m), g, 0, ctypes.byref(desc), None) == \
+        B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(dyn_m), fake, 0.0, t, None, None,
+                                 0, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(dyn_m), fake, 0.0, t, None, fake,
+                                 4096 * 4 - 1, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(dyn_m), fake, 0.0, t, None,
+                                 fake + 16, 1 << 20, None) == B.VDIT_ERR_BUFFER_TOO_SMALL  # not 256-byte aligned
+    # dynamic plan: pooled queries and keys, partial and final proxies, run and pair counts
+    m = B.mask_cfg("chunk_causal", 1)
+    assert L.vdit_plan_dynamic_workspace_bytes(ctypes.byref(m), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
+    nq, nk, hd = 3, 3, 2 * 64
+    a256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert n.value == (a256(nq * hd * 4) + a256(hd * nk * 4) + a256(nq * nk * 4 * 1) + a256(nq * nk * 4) +
+                       a256(nq * 4) + a256(nq * 8))
+    words = ctypes.c_size_t(0)
+    assert L.vdit_plan_dynamic_bound(ctypes.byref(m), g, 0, ctypes.byref(desc), ctypes.byref(words)) == 0
+    dyn = B.VditDynamicCfg(0.5, 0.0)
+    assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(desc), fake,
+                               words.value, None, fake, n.value - 1, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+    # relative L1: 8 bytes per 32768-element chunk and block
+    assert L.vdit_block_rel_l1_workspace_bytes(3, 70000, ctypes.byref(n)) == 0
+    assert n.value == 3 * 3 * 8
+    assert L.vdit_block_rel_l1_workspace_bytes(3, 0, ctypes.byref(n)) == 0 and n.value == 3 * 8
+    assert L.vdit_block_rel_l1_workspace_bytes(0, 64, ctypes.byref(n)) == B.VDIT_ERR_INVALID_ARG
+    out = 0x20000
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 3, 70000, 70000, out, fake, 71, None) == \
+        B.VDIT_ERR_BUFFER_TOO_SMALL
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 3, 70000, 70000, out, None, 1 << 20, None) == \
+        B.VDIT_ERR_BUFFER_TOO_SMALL
 
 
 def test_dynamic_plan_errors(L):
@@ -274,20 +325,20 @@ def test_dynamic_plan_errors(L):
     for tau in (-0.1, 1.5, float("nan")):
         dyn = B.VditDynamicCfg(tau, 0.0)
         assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(desc), fake,
-                                   words.value, None, None) == B.VDIT_ERR_INVALID_ARG
+                                   words.value, None, None, 0, None) == B.VDIT_ERR_INVALID_ARG
     dyn = B.VditDynamicCfg(0.5, 0.0)
     assert L.vdit_plan_dynamic(ctypes.byref(m), None, t, None, g, 0, ctypes.byref(desc), fake, words.value, None,
-                               None) == B.VDIT_ERR_INVALID_ARG
+                               None, 0, None) == B.VDIT_ERR_INVALID_ARG
     assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(desc), fake,
-                               words.value - 1, None, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+                               words.value - 1, None, None, 0, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
     many = np.full(4097, -1, np.int32)  # 4097 slots of one key tile each
     deep = B.VditKVCache(fake, fake, fake, many.ctypes.data, 4097, 24, 2, 64)
     assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(deep), fake,
-                               1 << 20, None, None) == B.VDIT_ERR_UNSUPPORTED
+                               1 << 20, None, None, 0, None) == B.VDIT_ERR_UNSUPPORTED
     # attention with the flag on a kind that does not exist
     bad = B.dynamic_mask(B.mask_cfg(7))
     assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(bad), fake, 0.0, t, None,
-                                 None) == B.VDIT_ERR_INVALID_ARG
+                                 None, 0, None) == B.VDIT_ERR_INVALID_ARG
 
 
 def test_reuse_policy_matches_oracle():
@@ -319,13 +370,13 @@ def test_reuse_policy_matches_oracle():
 def test_reuse_errors(L):
     fake = 0x10000  # never dereferenced: every call below fails validation first
     out = 0x20000
-    assert L.vdit_block_rel_l1(None, fake, B.VDIT_DTYPE_BF16, 2, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
-    assert L.vdit_block_rel_l1(fake, fake, 7, 2, 64, 64, out, None) == B.VDIT_ERR_UNSUPPORTED
-    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 0, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
-    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 70000, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
-    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 2, 64, 60, out, None) == B.VDIT_ERR_INVALID_ARG
-    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 2, 60, 60, out, None) == B.VDIT_ERR_INVALID_ARG
-    assert L.vdit_block_rel_l1(fake + 4, fake, B.VDIT_DTYPE_FP32, 2, 64, 64, out, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(None, fake, B.VDIT_DTYPE_BF16, 2, 64, 64, out, None, 0, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, 7, 2, 64, 64, out, None, 0, None) == B.VDIT_ERR_UNSUPPORTED
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 0, 64, 64, out, None, 0, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 70000, 64, 64, out, None, 0, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 2, 64, 60, out, None, 0, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake, fake, B.VDIT_DTYPE_BF16, 2, 60, 60, out, None, 0, None) == B.VDIT_ERR_INVALID_ARG
+    assert L.vdit_block_rel_l1(fake + 4, fake, B.VDIT_DTYPE_FP32, 2, 64, 64, out, None, 0, None) == B.VDIT_ERR_INVALID_ARG
     cfg = B.VditReuseCfg(0.1, 0, 10, 2)
     fr = ctypes.c_int32(-1)
     run = (ctypes.c_int32 * 2)()

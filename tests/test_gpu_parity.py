@@ -310,6 +310,40 @@ def test_fused_rope_and_standalone_rope_both_match_the_oracle():
         compare(b[:, h], a[:, h], what=f"standalone vs fused, head {h}")
 
 
+def test_two_streams_with_their_own_workspaces():
+    """Two chunks in flight at once on two streams, each with its own session (ring, plan and
+    caller-owned workspace, which the library only borrows): append, device plan and attention of
+    each match the oracle.  Nothing is synchronised between the two streams' calls."""
+    names = ["small_chunk_pad", "small_dense_d64"]  # unit-kernel plans: both use a workspace
+    cur = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for name, st in zip(names, streams):
+        w = get_workload(name)
+        inp = make_inputs(w)
+        dt = torch_dtype(w)
+        s = session_for(w, stream=st)
+        hist = [(t0, to_dev(hk, dt), to_dev(hv, dt)) for t0, f, hk, hv in inp["history"]]
+        k, v, q = to_dev(inp["k"], dt), to_dev(inp["v"], dt), to_dev(inp["q"], dt)
+        runs.append((w, inp, s, st, hist, k, v, q))
+    for w, inp, s, st, hist, k, v, q in runs:
+        st.wait_stream(cur)  # the inputs and the session's tables were made on the current stream
+    outs = []
+    for w, inp, s, st, hist, k, v, q in runs:  # both streams' work is enqueued before either is awaited
+        for t0, hk, hv in hist:
+            s.append(hk, hv, t0)
+        plan = s.append_plan(k, v, w.q_t0)
+        outs.append(s.attend(q, w.q_frames, w.q_t0, plan))
+    torch.cuda.synchronize()
+    for (w, inp, s, st, hist, k, v, q), o in zip(runs, outs):
+        assert s.attn_workspace.buf is not None
+        st_o = oracle.build_state(w, inp)
+        got = o.float().cpu().numpy()
+        for h in range(w.heads):
+            ref, _ = oracle.attention_rows(st_o, h)
+            compare(got[:, h], ref, what=f"{w.name} on its own stream, head {h}")
+
+
 def test_chunk_by_chunk_equals_whole_call():
     """Three 1-frame calls with global start frames give the 3-frame call's output."""
     w = get_workload("tiny")

@@ -51,8 +51,9 @@ def test_rel_l1_matches_oracle(dtype, shape):
         cd, pd = cur_p.cuda(), prev_p.cuda()
         out = torch.empty(shape[0] + 1, dtype=torch.float32, device="cuda")
         code = B.VDIT_DTYPE_BF16 if dtype == torch.bfloat16 else B.VDIT_DTYPE_FP32
+        ws = B.Workspace().get(B.vdit_block_rel_l1_workspace_bytes(shape[0], shape[1]))
         B._check(B.lib().vdit_block_rel_l1(cd.data_ptr(), pd.data_ptr(), code, shape[0], shape[1],
-                                           cd.stride(0), out.data_ptr(), B._stream(None)))
+                                           cd.stride(0), out.data_ptr(), ws.data_ptr(), ws.numel(), B._stream(None)))
     else:
         out = B.vdit_block_rel_l1(cur.cuda(), prev.cuda())
     torch.cuda.synchronize()

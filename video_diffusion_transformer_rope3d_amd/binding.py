@@ -28,6 +28,7 @@ EXPORTS = (
     "vdit_rope_table_build", "vdit_rope3d_qk", "vdit_kv_cache_bytes", "vdit_kv_cache_reset",
     "vdit_kv_append", "vdit_kv_append_plan", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
     "vdit_plan_dynamic", "vdit_block_attn_fwd", "vdit_block_rel_l1", "vdit_reuse_decide", "vdit_qkv_rope_append",
+    "vdit_block_attn_workspace_bytes", "vdit_plan_dynamic_workspace_bytes", "vdit_block_rel_l1_workspace_bytes",
 )
 
 
@@ -108,13 +109,18 @@ def lib():
                                               ctypes.POINTER(VditKVCache), pS]),
             "vdit_plan_dynamic": (I32, [ctypes.POINTER(VditMaskCfg), ctypes.POINTER(VditDynamicCfg), VditTensor,
                                         ctypes.POINTER(VditRopeCfg), VditGrid, I32, ctypes.POINTER(VditKVCache),
-                                        P, SZ, P, P]),
+                                        P, SZ, P, P, SZ, P]),
+            "vdit_plan_dynamic_workspace_bytes": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32,
+                                                        ctypes.POINTER(VditKVCache), pS]),
             "vdit_block_attn_fwd": (I32, [VditTensor, ctypes.POINTER(VditRopeCfg), VditGrid, I32,
                                           ctypes.POINTER(VditKVCache), ctypes.POINTER(VditMaskCfg), P,
-                                          ctypes.c_float, VditTensor, P, P]),
+                                          ctypes.c_float, VditTensor, P, P, SZ, P]),
+            "vdit_block_attn_workspace_bytes": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32,
+                                                      ctypes.POINTER(VditKVCache), pS]),
             "vdit_qkv_rope_append": (I32, [VditTensor, I32, P, ctypes.c_int64, P, ctypes.POINTER(VditRopeCfg),
                                            VditGrid, I32, ctypes.POINTER(VditKVCache), VditTensor, P]),
-            "vdit_block_rel_l1": (I32, [P, P, I32, I32, ctypes.c_int64, ctypes.c_int64, P, P]),
+            "vdit_block_rel_l1": (I32, [P, P, I32, I32, ctypes.c_int64, ctypes.c_int64, P, P, SZ, P]),
+            "vdit_block_rel_l1_workspace_bytes": (I32, [I32, ctypes.c_int64, pS]),
             "vdit_reuse_decide": (I32, [ctypes.POINTER(VditReuseCfg), I32, ctypes.c_float, ctypes.POINTER(I32),
                                         P, P]),
         }
@@ -307,18 +313,60 @@ def vdit_plan_dynamic_bound(base: VditMaskCfg, g: VditGrid, q_t0: int, cache: KV
     return n.value
 
 
+class Workspace:
+    """Caller-owned device scratch for the calls that need one (torch memory).  A buffer is
+    zeroed when it is allocated, which the attention call's counters require, and is only
+    replaced by a larger, zeroed one."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int, stream=None):
+        """The buffer, replaced by a zeroed one of at least nbytes if it is smaller; a new buffer
+        is allocated and zeroed on `stream` (torch's current stream when None), the stream of the
+        call that uses it."""
+        import torch
+        if self.buf is None or self.buf.numel() < nbytes:
+            if stream is None:
+                st = torch.cuda.current_stream()
+            elif isinstance(stream, torch.cuda.Stream):
+                st = stream
+            else:
+                st = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+            with torch.cuda.stream(st):
+                self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def ptr_size(self, nbytes: int, stream=None):
+        if nbytes == 0:
+            return None, 0
+        b = self.get(nbytes, stream)
+        return b.data_ptr(), b.numel()
+
+
+def vdit_plan_dynamic_workspace_bytes(base: VditMaskCfg, g: VditGrid, q_t0: int, cache: KVCache) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vdit_plan_dynamic_workspace_bytes(ctypes.byref(base), g, q_t0, ctypes.byref(cache.desc),
+                                                   ctypes.byref(n)))
+    return n.value
+
+
 def vdit_plan_dynamic(base: VditMaskCfg, tau: float, q, rope, g: VditGrid, q_t0: int, cache: KVCache,
-                      softmax_scale: float = 0.0, out=None, proxies=None, stream=None):
+                      softmax_scale: float = 0.0, out=None, proxies=None, stream=None, workspace=None):
     """Dynamic-threshold plan on the device (int32 tensor of the bound size; `out` reused if
-    given); `proxies`: optional fp32 device tensor [n_qtiles][key tiles] that receives them."""
+    given); `proxies`: optional fp32 device tensor [n_qtiles][key tiles] that receives them.
+    `workspace`: a Workspace (a new one for this call when None)."""
     import torch
     bound = vdit_plan_dynamic_bound(base, g, q_t0, cache)
     buf = torch.empty(bound, dtype=torch.int32, device="cuda") if out is None else out
     dyn = VditDynamicCfg(tau, softmax_scale)
     rp = ctypes.byref(rope.cfg) if rope is not None else None
+    ws = Workspace() if workspace is None else workspace
+    wp, wn = ws.ptr_size(vdit_plan_dynamic_workspace_bytes(base, g, q_t0, cache), stream)
     _check(lib().vdit_plan_dynamic(ctypes.byref(base), ctypes.byref(dyn), tensor(q), rp, g, q_t0,
                                    ctypes.byref(cache.desc), buf.data_ptr(), buf.numel(),
-                                   None if proxies is None else proxies.data_ptr(), _stream(stream)))
+                                   None if proxies is None else proxies.data_ptr(), wp, wn, _stream(stream)))
     return buf
 
 
@@ -329,14 +377,24 @@ def dynamic_mask(base: VditMaskCfg) -> VditMaskCfg:
     return m
 
 
+def vdit_block_attn_workspace_bytes(mask: VditMaskCfg, g: VditGrid, q_t0: int, cache: KVCache) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vdit_block_attn_workspace_bytes(ctypes.byref(mask), g, q_t0, ctypes.byref(cache.desc),
+                                                 ctypes.byref(n)))
+    return n.value
+
+
 def vdit_block_attn_fwd(q, rope, g: VditGrid, q_t0: int, cache: KVCache, mask: VditMaskCfg, plan_dev,
-                        softmax_scale: float = 0.0, o=None, lse=None, stream=None):
+                        softmax_scale: float = 0.0, o=None, lse=None, stream=None, workspace=None):
+    """`workspace`: a Workspace (a new, zeroed one for this call when None)."""
     import torch
     o = torch.empty_like(q) if o is None else o
     rp = ctypes.byref(rope.cfg) if rope is not None else None
+    ws = Workspace() if workspace is None else workspace
+    wp, wn = ws.ptr_size(vdit_block_attn_workspace_bytes(mask, g, q_t0, cache), stream)
     _check(lib().vdit_block_attn_fwd(tensor(q), rp, g, q_t0, ctypes.byref(cache.desc), ctypes.byref(mask),
                                      plan_dev.data_ptr(), ctypes.c_float(softmax_scale), tensor(o),
-                                     None if lse is None else lse.data_ptr(), _stream(stream)))
+                                     None if lse is None else lse.data_ptr(), wp, wn, _stream(stream)))
     return o
 
 
@@ -350,9 +408,16 @@ def plan_fields(plan):
     return p[:8], qt, rp, sp
 
 
-def vdit_block_rel_l1(cur, prev, out=None, stream=None):
+def vdit_block_rel_l1_workspace_bytes(n_blocks: int, block_elems: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vdit_block_rel_l1_workspace_bytes(n_blocks, block_elems, ctypes.byref(n)))
+    return n.value
+
+
+def vdit_block_rel_l1(cur, prev, out=None, stream=None, workspace=None):
     """Relative L1 distance of every block between two feature sets ([blocks][...] device
-    tensors, bf16 or fp32, rows contiguous) and their mean: fp32 tensor [blocks + 1]."""
+    tensors, bf16 or fp32, rows contiguous) and their mean: fp32 tensor [blocks + 1].
+    `workspace`: a Workspace (a new one for this call when None)."""
     import torch
     if cur.shape != prev.shape or cur.dtype != prev.dtype:
         raise ValueError("cur and prev must have one shape and dtype")
@@ -365,8 +430,10 @@ def vdit_block_rel_l1(cur, prev, out=None, stream=None):
         raise ValueError(f"unsupported dtype {cur.dtype}")
     out = torch.empty(nb + 1, dtype=torch.float32, device=cur.device) if out is None else out
     stride = cur2.stride(0) if cur2.shape[1] > 0 else 0  # empty blocks: nothing is read
+    ws = Workspace(cur.device) if workspace is None else workspace
+    b = ws.get(vdit_block_rel_l1_workspace_bytes(nb, cur2.shape[1]), stream)
     _check(lib().vdit_block_rel_l1(cur2.data_ptr(), prev2.data_ptr(), dt, nb, cur2.shape[1], stride,
-                                   out.data_ptr(), _stream(stream)))
+                                   out.data_ptr(), b.data_ptr(), b.numel(), _stream(stream)))
     return out
 
 

@@ -422,9 +422,20 @@ int vdit_plan_dynamic_bound(const vdit_mask_cfg* base, vdit_grid q_grid, int32_t
     return ok();
 }
 
+int vdit_plan_dynamic_workspace_bytes(const vdit_mask_cfg* base, vdit_grid q_grid, int32_t q_t0,
+                                      const vdit_kv_cache* cache, size_t* bytes) {
+    int st = check_plan_args(base, q_grid, q_t0, cache);
+    if (st) return st;
+    if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
+    if (!bytes) return fail(VDIT_ERR_INVALID_ARG, "bytes is NULL");
+    PlanGeom g = make_geom(base, q_grid, q_t0, cache);
+    *bytes = dyn_workspace_bytes(g, plan_qtile_count(g), cache->heads, cache->head_dim);
+    return ok();
+}
+
 int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vdit_tensor q, const vdit_rope_cfg* rope,
                       vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache, int32_t* plan_dev, size_t cap_words,
-                      float* proxies_dev, void* stream) {
+                      float* proxies_dev, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_plan_args(base, q_grid, q_t0, cache);
     if (st) return st;
     if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
@@ -442,7 +453,12 @@ int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vd
     const size_t need = plan_bound_words(nq, cache->capacity * ceil_div(g.hw, g.tile));
     if (cap_words < need)
         return fail(VDIT_ERR_BUFFER_TOO_SMALL, "plan buffer holds %zu words, the bound is %zu", cap_words, need);
+    const size_t ws_need = dyn_workspace_bytes(g, nq, cache->heads, cache->head_dim);
+    if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255))
+        return fail(VDIT_ERR_BUFFER_TOO_SMALL, "workspace %p of %zu bytes; the call needs %zu bytes, 256-byte aligned",
+                    workspace, workspace_bytes, ws_need);
     DynLaunch a{};
+    a.workspace = workspace;
     if (rope) {
         if ((st = check_rope_use(rope, cache->head_dim, q_grid, q_t0))) return st;
         a.rope = rope_dev(rope);
@@ -466,19 +482,58 @@ int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vd
     return device_status(launch_plan_dynamic(a, (hipStream_t)stream), "dynamic plan kernels");
 }
 
+namespace {
+// The rule of an attention call: a plan from vdit_plan_dynamic is marked in the kind, and the
+// geometry is the base rule's.
+struct AttnRule {
+    vdit_mask_cfg base{};
+    const vdit_mask_cfg* mask = nullptr;
+    bool dynamic = false;
+};
+AttnRule attn_rule(const vdit_mask_cfg* mask_in) {
+    AttnRule r;
+    r.mask = mask_in;
+    if (mask_in && (mask_in->kind & VDIT_MASK_FLAG_DYNAMIC)) {
+        r.base = *mask_in;
+        r.base.kind &= ~VDIT_MASK_FLAG_DYNAMIC;
+        r.mask = &r.base;
+        r.dynamic = true;
+    }
+    return r;
+}
+
+// Workspace bytes of an attention call on the current device (arguments already checked).
+int attn_ws_need(const vdit_mask_cfg* mask, bool dynamic, int32_t heads, int32_t n_qtiles, size_t* need) {
+    const bool unit = !attn_uses_tile_kernel(mask->kind, dynamic);
+    int grid = 0;
+    if (unit) {
+        hipError_t e = attn_unit_grid(&grid);
+        if (e != hipSuccess) return device_status(e, "device attribute query");
+    }
+    *need = attn_workspace_bytes(grid, heads, n_qtiles, unit, dynamic);
+    return VDIT_OK;
+}
+}  // namespace
+
+int vdit_block_attn_workspace_bytes(const vdit_mask_cfg* mask_in, vdit_grid q_grid, int32_t q_t0,
+                                    const vdit_kv_cache* cache, size_t* bytes) {
+    const AttnRule r = attn_rule(mask_in);
+    int st = check_plan_args(r.mask, q_grid, q_t0, cache);
+    if (st) return st;
+    if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
+    if (!bytes) return fail(VDIT_ERR_INVALID_ARG, "bytes is NULL");
+    PlanGeom g = make_geom(r.mask, q_grid, q_t0, cache);
+    if ((st = attn_ws_need(r.mask, r.dynamic, cache->heads, plan_qtile_count(g), bytes))) return st;
+    return ok();
+}
+
 int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
                         const vdit_kv_cache* cache, const vdit_mask_cfg* mask_in, const int32_t* plan_dev,
-                        float softmax_scale, vdit_tensor o, float* lse, void* stream) {
-    // a plan from vdit_plan_dynamic is marked in the kind; the geometry is the base rule's
-    vdit_mask_cfg mask_base{};
-    const vdit_mask_cfg* mask = mask_in;
-    bool unpaired = false;
-    if (mask_in && (mask_in->kind & VDIT_MASK_FLAG_DYNAMIC)) {
-        mask_base = *mask_in;
-        mask_base.kind &= ~VDIT_MASK_FLAG_DYNAMIC;
-        mask = &mask_base;
-        unpaired = true;
-    }
+                        float softmax_scale, vdit_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    const AttnRule rule = attn_rule(mask_in);
+    const vdit_mask_cfg* mask = rule.mask;
+    const bool unpaired = rule.dynamic;
     int st = check_plan_args(mask, q_grid, q_t0, cache);
     if (st) return st;
     if (!cache) return fail(VDIT_ERR_INVALID_ARG, "cache is NULL");
@@ -517,11 +572,25 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
     if (a.n_qtiles > kAttnMaxQTiles)
         return fail(VDIT_ERR_UNSUPPORTED, "%d query tiles in one call; at most %d (split the call by frames)",
                     a.n_qtiles, kAttnMaxQTiles);
+    size_t ws_need = 0;
+    if ((st = attn_ws_need(mask, unpaired, cache->heads, a.n_qtiles, &ws_need))) return st;
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255)))
+        return fail(VDIT_ERR_BUFFER_TOO_SMALL, "workspace %p of %zu bytes; the call needs %zu bytes, 256-byte aligned",
+                    workspace, workspace_bytes, ws_need);
+    a.workspace = workspace;
     return device_status(launch_attn_fwd(a, (hipStream_t)stream), "attention kernel");
 }
 
+int vdit_block_rel_l1_workspace_bytes(int32_t n_blocks, int64_t block_elems, size_t* bytes) {
+    if (!bytes) return fail(VDIT_ERR_INVALID_ARG, "bytes is NULL");
+    if (n_blocks < 1 || n_blocks > 65535) return fail(VDIT_ERR_INVALID_ARG, "n_blocks %d outside [1, 65535]", n_blocks);
+    if (block_elems < 0) return fail(VDIT_ERR_INVALID_ARG, "block_elems %lld < 0", (long long)block_elems);
+    *bytes = rel_l1_workspace_bytes(n_blocks, block_elems);
+    return ok();
+}
+
 int vdit_block_rel_l1(const void* cur, const void* prev, int32_t dtype, int32_t n_blocks, int64_t block_elems,
-                      int64_t block_stride, float* out_dev, void* stream) {
+                      int64_t block_stride, float* out_dev, void* workspace, size_t workspace_bytes, void* stream) {
     if (!out_dev) return fail(VDIT_ERR_INVALID_ARG, "out is NULL");
     if (block_elems > 0 && (!cur || !prev)) return fail(VDIT_ERR_INVALID_ARG, "cur and prev must be set");
     if (dtype != VDIT_DTYPE_BF16 && dtype != VDIT_DTYPE_FP32)
@@ -535,8 +604,12 @@ int vdit_block_rel_l1(const void* cur, const void* prev, int32_t dtype, int32_t 
     if (((uintptr_t)cur & 15) || ((uintptr_t)prev & 15))
         return fail(VDIT_ERR_INVALID_ARG, "feature pointers must be 16-byte aligned");
     if (((uintptr_t)out_dev & 3)) return fail(VDIT_ERR_INVALID_ARG, "out not 4-byte aligned");
+    const size_t ws_need = rel_l1_workspace_bytes(n_blocks, block_elems);
+    if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 15))
+        return fail(VDIT_ERR_BUFFER_TOO_SMALL, "workspace %p of %zu bytes; the call needs %zu bytes, 16-byte aligned",
+                    workspace, workspace_bytes, ws_need);
     return device_status(launch_rel_l1(cur, prev, dtype == VDIT_DTYPE_FP32, n_blocks, block_elems, block_stride,
-                                       out_dev, (hipStream_t)stream),
+                                       out_dev, workspace, (hipStream_t)stream),
                          "relative L1 kernels");
 }
 

@@ -24,8 +24,6 @@
 // MFMA is chosen (bits 2 and 3 of the S row index swapped) so that the bf16 P operand is
 // taken from the S accumulator registers as they are and V^T is read from LDS with one
 // 16-byte read per lane.
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1274,105 +1272,53 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     }
 }
 
-// Workspace of one (device, stream).  Counters and partials are separate buffers: every
-// word that has ever served as a counter is zero between calls (the last arriver of a tile
-// resets its counter), which would not hold if the two regions shifted between calls.
-struct Workspace {
-    int32_t* cnt = nullptr;
-    size_t cnt_words = 0;
-    float* part = nullptr;
-    size_t part_floats = 0;
-    int32_t* order = nullptr;  // tile kernel order (rewritten by every call that uses it)
-    size_t order_words = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Workspace layout (caller-owned, see vdit_block_attn_workspace_bytes): the tile order of
+// dynamic plans (kMaxTiles words), then the split-unit partials (two slots per workgroup, sized
+// for head_dim 128 whatever the call's), then the per-tile arrival counters.  Every region
+// starts at an offset that depends on the device only, so a word that served as a counter is
+// never reused as anything else and stays zero between calls (the last arriver of a tile resets
+// its counter); the caller zeroes the workspace once.
+constexpr size_t kOrderBytes = (size_t)kMaxTiles * 4;
 
-template <typename X>
-hipError_t grow(X*& p, size_t& have, size_t need, bool zero, hipStream_t s) {
-    if (have >= need) return hipSuccess;
-    hipError_t e;
-    if (p) {  // the old buffer may still be in use by this stream's previous launch
-        if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-        if ((e = hipFree(p)) != hipSuccess) return e;
-        p = nullptr;
-        have = 0;
-    }
-    if ((e = hipMalloc(reinterpret_cast<void**>(&p), need * sizeof(X))) != hipSuccess) return e;
-    if (zero) {
-        if ((e = hipMemset(p, 0, need * sizeof(X))) != hipSuccess) return e;
-        if ((e = hipDeviceSynchronize()) != hipSuccess) return e;  // zeroed before any stream uses it
-    }
-    have = need;
-    return hipSuccess;
-}
+size_t partial_bytes(int grid) { return (size_t)2 * grid * Partial<128>::SLOT * 4; }
 
-hipError_t workspace_for(hipStream_t s, size_t cnt_words, size_t part_floats, int32_t** cnt, float** part) {
-    int dev = 0;
+}  // namespace
+
+// Workgroups of the unit kernel: one per CU (its LDS admits no second), a multiple of 8 so
+// that the XCD renumbering is exact.
+hipError_t attn_unit_grid(int* grid) {
+    int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[{dev, s}];
-    if ((e = grow(w.cnt, w.cnt_words, cnt_words, true, s)) != hipSuccess) return e;
-    if ((e = grow(w.part, w.part_floats, part_floats, false, s)) != hipSuccess) return e;
-    *cnt = w.cnt;
-    *part = w.part;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    *grid = cus / 8 * 8 < 8 ? 8 : cus / 8 * 8;
     return hipSuccess;
 }
 
-struct GridInfo {
-    int cus = 0;
-    int per_cu[2][2][2] = {};  // unit kernel, [D == 128][QF32][OF32]
-};
-std::mutex g_grid_mutex;
-std::map<int, GridInfo> g_grid;
+size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool order) {
+    if (unit_kernel) return kOrderBytes + partial_bytes(grid) + (size_t)heads * n_qtiles * 4;
+    return order ? kOrderBytes : 0;
+}
+
+namespace {
 
 template <int D, bool QF, bool OF>
-hipError_t launch_unit(AttnArgs a, int n_heads_tiles, hipStream_t s) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+hipError_t launch_unit(AttnArgs a, char* ws, hipStream_t s) {
+    int grid = 0;
+    hipError_t e = attn_unit_grid(&grid);
     if (e != hipSuccess) return e;
-    int cus, per_cu;
-    {
-        std::lock_guard<std::mutex> lock(g_grid_mutex);
-        GridInfo& gi = g_grid[dev];
-        if (gi.cus == 0 &&
-            (e = hipDeviceGetAttribute(&gi.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-            return e;
-        int& pc = gi.per_cu[D == 128][QF][OF];
-        if (pc == 0 && (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, attn_unit_kernel<D, QF, OF>,
-                                                                         kUnitWaves * 64, 0)) != hipSuccess)
-            return e;
-        cus = gi.cus;
-        per_cu = pc < 1 ? 1 : pc;
-    }
-    const int grid = ((cus * per_cu) / 8 < 1 ? 1 : (cus * per_cu) / 8) * 8;
-    if ((e = workspace_for(s, (size_t)n_heads_tiles, (size_t)2 * grid * Partial<D>::SLOT, &a.cnt, &a.part)) !=
-        hipSuccess)
-        return e;
+    a.part = reinterpret_cast<float*>(ws + kOrderBytes);
+    a.cnt = reinterpret_cast<int32_t*>(ws + kOrderBytes + partial_bytes(grid));
     attn_unit_kernel<D, QF, OF><<<grid, kUnitWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t order_workspace(hipStream_t s, size_t words, int32_t** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[{dev, s}];
-    if ((e = grow(w.order, w.order_words, words, false, s)) != hipSuccess) return e;
-    *out = w.order;
-    return hipSuccess;
-}
-
 template <int D, bool QF, bool OF>
-hipError_t launch_tile(AttnArgs a, bool longest_first, hipStream_t s) {
+hipError_t launch_tile(AttnArgs a, bool longest_first, char* ws, hipStream_t s) {
     const unsigned blocks = (unsigned)(a.n_qtiles * a.heads);
     a.order = nullptr;
     if (longest_first) {
-        int32_t* order = nullptr;
-        hipError_t e = order_workspace(s, (size_t)a.n_qtiles, &order);
-        if (e != hipSuccess) return e;
+        int32_t* order = reinterpret_cast<int32_t*>(ws);
         tile_order_kernel<<<1, kOrderThreads, 0, s>>>(a.plan, a.n_qtiles, order);
         a.order = order;
     }
@@ -1382,10 +1328,9 @@ hipError_t launch_tile(AttnArgs a, bool longest_first, hipStream_t s) {
 
 template <int D, bool QF, bool OF>
 hipError_t launch_k(const AttnLaunch& L, const AttnArgs& a, hipStream_t s) {
-    // neighbouring log-radial tiles (and tiles of dynamic plans) do not share span lists:
-    // one tile per workgroup
-    if (is_radial(L.mask_kind) || L.unpaired) return launch_tile<D, QF, OF>(a, L.unpaired, s);
-    return launch_unit<D, QF, OF>(a, L.n_qtiles * L.heads, s);
+    char* ws = static_cast<char*>(L.workspace);
+    if (attn_uses_tile_kernel(L.mask_kind, L.unpaired)) return launch_tile<D, QF, OF>(a, L.unpaired, ws, s);
+    return launch_unit<D, QF, OF>(a, ws, s);
 }
 
 template <int D>

@@ -14,8 +14,6 @@
 // [nq][nk] (a small fp32 product), then per query tile the threshold and the run count,
 // and per query tile its offset (a sum over the counts before it) and its runs.
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <utility>
 
 #include "vdit_bf16.hpp"
@@ -429,54 +427,47 @@ __global__ __launch_bounds__(kDynThreads) void dyn_write_kernel(PlanGeom g, cons
     }
 }
 
-// Scratch of one (device, stream): pooled queries, pooled keys, proxies, run and pair counts.
-struct DynWorkspace {
-    char* ptr = nullptr;
-    size_t bytes = 0;
-};
-std::mutex g_dyn_mutex;
-std::map<std::pair<int, hipStream_t>, DynWorkspace> g_dyn_ws;
-
-hipError_t dyn_workspace(hipStream_t s, size_t bytes, char** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_dyn_mutex);
-    DynWorkspace& w = g_dyn_ws[{dev, s}];
-    if (w.bytes < bytes) {
-        if (w.ptr) {  // the old buffer may still be in use by this stream's previous launch
-            if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-            if ((e = hipFree(w.ptr)) != hipSuccess) return e;
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        if ((e = hipMalloc(reinterpret_cast<void**>(&w.ptr), bytes)) != hipSuccess) return e;
-        w.bytes = bytes;
-    }
-    *out = w.ptr;
-    return hipSuccess;
-}
-
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Partial proxies are kept under this many bytes: the channels are split over as many
 // slices (whole heads) as fit, at most one per head.
 constexpr size_t kPartBytes = size_t(64) << 20;
 
+// Sizes of the workspace regions: pooled queries, pooled keys (transposed), partial proxies,
+// proxies (when the caller does not take them), run and pair counts per query tile.
+struct DynSizes {
+    int32_t cps, slices;
+    size_t qbar, kbar, part, prox, runs, pairs;
+    size_t total() const { return qbar + kbar + part + prox + runs + pairs; }
+};
+
+DynSizes dyn_sizes(const PlanGeom& g, int32_t nq, int32_t heads, int32_t head_dim) {
+    const int32_t hd = heads * head_dim;
+    const int32_t nk = g.capacity * ceil_div(g.hw, g.tile);
+    const size_t one = (size_t)nq * nk * 4;
+    const int32_t want = (int32_t)std::max<size_t>(1, std::min<size_t>((size_t)heads, kPartBytes / one));
+    DynSizes z;
+    z.cps = ceil_div(heads, want) * head_dim;
+    z.slices = ceil_div(hd, z.cps);
+    z.qbar = align256((size_t)nq * hd * 4);
+    z.kbar = align256((size_t)hd * nk * 4);
+    z.part = align256(one * z.slices);
+    z.prox = align256(one);
+    z.runs = align256((size_t)nq * 4);
+    z.pairs = align256((size_t)nq * 8);
+    return z;
+}
+
 template <int D>
 hipError_t launch_dyn_d(const DynLaunch& L, hipStream_t s) {
     const PlanGeom& g = L.geom;
     const int32_t nq = L.n_qtiles, heads = L.heads, hd = heads * D;
     const int32_t nk = g.capacity * ceil_div(g.hw, g.tile);
-    const size_t one = (size_t)nq * nk * 4;
-    const int32_t want = (int32_t)std::max<size_t>(1, std::min<size_t>((size_t)heads, kPartBytes / one));
-    const int32_t cps = ceil_div(heads, want) * D, slices = ceil_div(hd, cps);
-    const size_t b_qbar = align256((size_t)nq * hd * 4), b_kbar = align256((size_t)hd * nk * 4);
-    const size_t b_part = align256(one * slices), b_prox = L.proxies ? 0 : align256(one);
-    const size_t b_runs = align256((size_t)nq * 4), b_pairs = align256((size_t)nq * 8);
-    char* ws = nullptr;
-    hipError_t e = dyn_workspace(s, b_qbar + b_kbar + b_part + b_prox + b_runs + b_pairs, &ws);
-    if (e != hipSuccess) return e;
+    const DynSizes z = dyn_sizes(g, nq, heads, D);
+    const int32_t cps = z.cps, slices = z.slices;
+    const size_t b_qbar = z.qbar, b_kbar = z.kbar, b_part = z.part, b_prox = z.prox, b_runs = z.runs,
+                 b_pairs = z.pairs;
+    char* ws = static_cast<char*>(L.workspace);
     char* at = ws;
     auto take = [&](size_t b) {
         char* p = at;
@@ -486,7 +477,8 @@ hipError_t launch_dyn_d(const DynLaunch& L, hipStream_t s) {
     float* qbar = reinterpret_cast<float*>(take(b_qbar));
     float* kbar_t = reinterpret_cast<float*>(take(b_kbar));
     float* part = reinterpret_cast<float*>(take(b_part));
-    float* prox = L.proxies ? L.proxies : reinterpret_cast<float*>(take(b_prox));
+    float* prox = reinterpret_cast<float*>(take(b_prox));
+    if (L.proxies) prox = L.proxies;
     int32_t* runs = reinterpret_cast<int32_t*>(take(b_runs));
     long long* pairs = reinterpret_cast<long long*>(take(b_pairs));
     const uint16_t* kc = static_cast<const uint16_t*>(L.kc);
@@ -507,6 +499,10 @@ hipError_t launch_dyn_d(const DynLaunch& L, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t dyn_workspace_bytes(const PlanGeom& g, int32_t n_qtiles, int32_t heads, int32_t head_dim) {
+    return dyn_sizes(g, n_qtiles, heads, head_dim).total();
+}
 
 hipError_t launch_plan_dynamic(const DynLaunch& L, hipStream_t s) {
     if (L.head_dim == 128) return launch_dyn_d<128>(L, s);

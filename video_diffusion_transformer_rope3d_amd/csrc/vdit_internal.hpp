@@ -225,6 +225,7 @@ struct AttnLaunch {
     int32_t mask_kind;
     bool unpaired;  // plan from vdit_plan_dynamic: neighbouring tiles do not share span lists
     float scale_log2;
+    void* workspace;  // caller-owned, attn_workspace_bytes
 };
 struct DynLaunch {
     PlanGeom geom;  // static rule of the call (candidates and query tiles)
@@ -238,6 +239,7 @@ struct DynLaunch {
     float scale, keep_frac;  // keep_frac = 1 - tau
     float* proxies;          // optional [n_qtiles][capacity * tiles per frame]
     int32_t* plan;
+    void* workspace;         // caller-owned, dyn_workspace_bytes
 };
 hipError_t launch_plan_dynamic(const DynLaunch& a, hipStream_t s);
 // Fused QKV projection + RoPE + K/V append (validated by the caller).
@@ -266,12 +268,22 @@ hipError_t launch_qkv_rope_append(const ProjLaunch& L, hipStream_t s);
 // tokens of those slots (when frames are padded), as the append does.
 hipError_t launch_kv_zero_pad(const vdit_kv_cache& c, vdit_grid grid, int32_t t0, hipStream_t s);
 hipError_t launch_rel_l1(const void* cur, const void* prev, bool f32, int32_t n_blocks, int64_t block_elems,
-                         int64_t block_stride, float* out, hipStream_t s);
+                         int64_t block_stride, float* out, void* workspace, hipStream_t s);
 
 // Query tiles one attention call can hold (its unit table lives in LDS).
 constexpr int32_t kAttnMaxQTiles = 4096;
 // key tiles (cache slots x tiles per frame) one dynamic plan may weigh
 constexpr int32_t kDynMaxKeyTiles = 4096;
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t s);
+// Neighbouring log-radial query tiles (and the tiles of dynamic plans) do not share span
+// lists: those plans run one tile per workgroup; chunk-causal and dense plans pair tiles
+// into units.
+inline bool attn_uses_tile_kernel(int32_t mask_kind, bool unpaired) { return is_radial(mask_kind) || unpaired; }
+// Grid of the unit kernel on the current device, and the workspace a call needs.
+hipError_t attn_unit_grid(int* grid);
+size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool order);
+// Workspace of vdit_plan_dynamic and of vdit_block_rel_l1 (bytes).
+size_t dyn_workspace_bytes(const PlanGeom& g, int32_t n_qtiles, int32_t heads, int32_t head_dim);
+size_t rel_l1_workspace_bytes(int32_t n_blocks, int64_t block_elems);
 
 }  // namespace vdit

@@ -8,8 +8,6 @@
 // sums |cur - prev| and |prev| over one chunk of one block in fp32 (per-thread runs, then a
 // tree over the workgroup).  Pass 2: one workgroup adds each block's chunk sums in fp64 in a
 // fixed order (deterministic, no atomics), divides, and averages over the blocks.
-#include <map>
-#include <mutex>
 #include <utility>
 
 #include "vdit_internal.hpp"
@@ -144,43 +142,18 @@ __global__ __launch_bounds__(kFinalThreads) void rel_l1_final_kernel(const float
     }
 }
 
-struct ReuseWorkspace {
-    float2* ptr = nullptr;
-    size_t n = 0;
-};
-std::mutex g_reuse_mutex;
-std::map<std::pair<int, hipStream_t>, ReuseWorkspace> g_reuse_ws;
-
-hipError_t reuse_workspace(hipStream_t s, size_t n, float2** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_reuse_mutex);
-    ReuseWorkspace& w = g_reuse_ws[{dev, s}];
-    if (w.n < n) {
-        if (w.ptr) {  // the old buffer may still be in use by this stream's previous launch
-            if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-            if ((e = hipFree(w.ptr)) != hipSuccess) return e;
-            w.ptr = nullptr;
-            w.n = 0;
-        }
-        if ((e = hipMalloc(reinterpret_cast<void**>(&w.ptr), n * sizeof(float2))) != hipSuccess) return e;
-        w.n = n;
-    }
-    *out = w.ptr;
-    return hipSuccess;
-}
-
 }  // namespace
 
 int64_t rel_l1_chunks(int64_t block_elems) { return block_elems > 0 ? (block_elems + kChunk - 1) / kChunk : 1; }
 
+size_t rel_l1_workspace_bytes(int32_t n_blocks, int64_t block_elems) {
+    return (size_t)rel_l1_chunks(block_elems) * n_blocks * sizeof(float2);
+}
+
 hipError_t launch_rel_l1(const void* cur, const void* prev, bool f32, int32_t n_blocks, int64_t block_elems,
-                         int64_t block_stride, float* out, hipStream_t s) {
+                         int64_t block_stride, float* out, void* workspace, hipStream_t s) {
     const int32_t chunks = (int32_t)rel_l1_chunks(block_elems);
-    float2* part = nullptr;
-    hipError_t e = reuse_workspace(s, (size_t)chunks * n_blocks, &part);
-    if (e != hipSuccess) return e;
+    float2* part = static_cast<float2*>(workspace);
     const dim3 grid(chunks, n_blocks);
     if (f32)
         rel_l1_partial_kernel<true><<<grid, kReuseThreads, 0, s>>>(cur, prev, block_elems, block_stride, chunks, part);

@@ -9,7 +9,8 @@ Convenience over the C ABI for the usual call sequence of a denoising chunk:
     plan = s.plan(q_frames=3, q_t0=t0)  # block list on the device
     o = s.attend(q, q_frames=3, q_t0=t0, plan=plan)
 
-Device memory comes from torch; every computation is a libvdit kernel.
+Device memory comes from torch (the ring, tables, outputs and the session's workspace, zeroed
+when allocated); every computation is a libvdit kernel.
 """
 from __future__ import annotations
 
@@ -26,6 +27,10 @@ class AttentionSession:
         self.rope = B.Rope(head_dim, rope_dims, theta, max_t, frame_h, frame_w, device=device)
         self.cache = B.KVCache(capacity, frame_h * frame_w, heads, head_dim, device=device, stream=stream)
         self.mask = B.mask_cfg(mask, chunk_frames, tile, radial_w0, radial_decay_log2, long_range_period)
+        # workspaces of the session's calls, which run in order on its stream: attention (whose
+        # counters must stay zero between calls) and the dynamic plan have one each
+        self.attn_workspace = B.Workspace(device)
+        self.dyn_workspace = B.Workspace(device)
 
     def grid(self, frames):
         return B.grid(frames, self.frame_h, self.frame_w)
@@ -51,9 +56,10 @@ class AttentionSession:
         """`mask`: the session's rule by default; B.dynamic_mask(session.mask) for a plan from
         plan_dynamic."""
         return B.vdit_block_attn_fwd(q, self.rope if rotate else None, self.grid(q_frames), q_t0, self.cache,
-                                     self.mask if mask is None else mask, plan, softmax_scale, o, lse, self.stream)
+                                     self.mask if mask is None else mask, plan, softmax_scale, o, lse, self.stream,
+                                     self.attn_workspace)
 
     def plan_dynamic(self, q, q_frames, q_t0, tau, out=None, proxies=None, rotate=True, softmax_scale=0.0):
         """Dynamic-threshold plan of the session's rule on the device."""
         return B.vdit_plan_dynamic(self.mask, tau, q, self.rope if rotate else None, self.grid(q_frames), q_t0,
-                                   self.cache, softmax_scale, out, proxies, self.stream)
+                                   self.cache, softmax_scale, out, proxies, self.stream, self.dyn_workspace)
