@@ -17,7 +17,9 @@
  *   workspaces of vdit_block_attn_fwd, vdit_plan_dynamic and vdit_block_rel_l1 included
  *   (each has a *_workspace_bytes size query).  Pointers documented "device" must be device
  *   memory of the current HIP device, "host" plain host memory.  The library allocates no
- *   memory and keeps no global state besides a per-thread error string.
+ *   memory and keeps no global state besides a per-thread error string, except the one entry
+ *   point for callers that cannot allocate (vdit_block_attn_fwd_static), whose static device
+ *   scratch array is documented there.
  * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
  *   work is only enqueued; no call synchronises the device or a stream.  Calls that may run
  *   at the same time must not share a workspace.
@@ -293,6 +295,19 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
                         const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
                         float softmax_scale, vdit_tensor o, float* lse, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* vdit_block_attn_fwd_static: vdit_block_attn_fwd with no workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It allocates nothing: its scratch is a static device array of
+ * 72 MiB on each GPU the library runs on, held until the process ends.  Before each call it
+ * clears the part that must start at zero (the arrival counters) with a small fill kernel on
+ * `stream`.  Every call on a GPU shares that GPU's array: calls that may overlap on one GPU
+ * (other streams, other host threads) race and must not be issued.  Arguments and results
+ * as for vdit_block_attn_fwd; a call whose workspace size query exceeds 72 MiB (a grid of
+ * far more CUs, or more than about 1.5 million head x query-tile counters) -> UNSUPPORTED. */
+int vdit_block_attn_fwd_static(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
+                               const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
+                               float softmax_scale, vdit_tensor o, float* lse, void* stream);
 
 /* ---- fused QKV projection + RoPE3D + K/V append ("Accelerating Video Generation Inference ...",
  * section 2.C, the QKV projection and the rotary embedding as one kernel with precomputed

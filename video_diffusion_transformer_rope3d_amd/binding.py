@@ -29,6 +29,7 @@ EXPORTS = (
     "vdit_kv_append", "vdit_kv_append_plan", "vdit_plan_qtiles", "vdit_plan_bound", "vdit_plan_mask", "vdit_plan_dynamic_bound",
     "vdit_plan_dynamic", "vdit_block_attn_fwd", "vdit_block_rel_l1", "vdit_reuse_decide", "vdit_qkv_rope_append",
     "vdit_block_attn_workspace_bytes", "vdit_plan_dynamic_workspace_bytes", "vdit_block_rel_l1_workspace_bytes",
+    "vdit_block_attn_fwd_static",
 )
 
 
@@ -117,6 +118,9 @@ def lib():
                                           ctypes.c_float, VditTensor, P, P, SZ, P]),
             "vdit_block_attn_workspace_bytes": (I32, [ctypes.POINTER(VditMaskCfg), VditGrid, I32,
                                                       ctypes.POINTER(VditKVCache), pS]),
+            "vdit_block_attn_fwd_static": (I32, [VditTensor, ctypes.POINTER(VditRopeCfg), VditGrid, I32,
+                                                 ctypes.POINTER(VditKVCache), ctypes.POINTER(VditMaskCfg), P,
+                                                 ctypes.c_float, VditTensor, P, P]),
             "vdit_qkv_rope_append": (I32, [VditTensor, I32, P, ctypes.c_int64, P, ctypes.POINTER(VditRopeCfg),
                                            VditGrid, I32, ctypes.POINTER(VditKVCache), VditTensor, P]),
             "vdit_block_rel_l1": (I32, [P, P, I32, I32, ctypes.c_int64, ctypes.c_int64, P, P, SZ, P]),
@@ -395,6 +399,19 @@ def vdit_block_attn_fwd(q, rope, g: VditGrid, q_t0: int, cache: KVCache, mask: V
     _check(lib().vdit_block_attn_fwd(tensor(q), rp, g, q_t0, ctypes.byref(cache.desc), ctypes.byref(mask),
                                      plan_dev.data_ptr(), ctypes.c_float(softmax_scale), tensor(o),
                                      None if lse is None else lse.data_ptr(), wp, wn, _stream(stream)))
+    return o
+
+
+def vdit_block_attn_fwd_static(q, rope, g: VditGrid, q_t0: int, cache: KVCache, mask: VditMaskCfg, plan_dev,
+                               softmax_scale: float = 0.0, o=None, lse=None, stream=None):
+    """vdit_block_attn_fwd on the library's static scratch (no workspace, nothing allocated by
+    the library; `o` is allocated here when None)."""
+    import torch
+    o = torch.empty_like(q) if o is None else o
+    rp = ctypes.byref(rope.cfg) if rope is not None else None
+    _check(lib().vdit_block_attn_fwd_static(tensor(q), rp, g, q_t0, ctypes.byref(cache.desc), ctypes.byref(mask),
+                                            plan_dev.data_ptr(), ctypes.c_float(softmax_scale), tensor(o),
+                                            None if lse is None else lse.data_ptr(), _stream(stream)))
     return o
 
 

@@ -527,10 +527,12 @@ int vdit_block_attn_workspace_bytes(const vdit_mask_cfg* mask_in, vdit_grid q_gr
     return ok();
 }
 
-int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
-                        const vdit_kv_cache* cache, const vdit_mask_cfg* mask_in, const int32_t* plan_dev,
-                        float softmax_scale, vdit_tensor o, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+namespace {
+// vdit_block_attn_fwd with the caller's workspace, or (static_scratch) with the library's
+// static scratch array of this device.
+int attn_fwd_impl(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0, const vdit_kv_cache* cache,
+                  const vdit_mask_cfg* mask_in, const int32_t* plan_dev, float softmax_scale, vdit_tensor o, float* lse,
+                  void* workspace, size_t workspace_bytes, bool static_scratch, void* stream) {
     const AttnRule rule = attn_rule(mask_in);
     const vdit_mask_cfg* mask = rule.mask;
     const bool unpaired = rule.dynamic;
@@ -574,11 +576,46 @@ int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_gr
                     a.n_qtiles, kAttnMaxQTiles);
     size_t ws_need = 0;
     if ((st = attn_ws_need(mask, unpaired, cache->heads, a.n_qtiles, &ws_need))) return st;
+    if (static_scratch) {
+        if (ws_need > kAttnStaticScratchBytes)
+            return fail(VDIT_ERR_UNSUPPORTED, "the call needs %zu bytes of scratch; the static scratch holds %zu",
+                        ws_need, kAttnStaticScratchBytes);
+        hipError_t e = attn_static_scratch(&workspace);
+        if (e != hipSuccess) return device_status(e, "static scratch address");
+        workspace_bytes = kAttnStaticScratchBytes;
+        // the unit kernel's arrival counters must start at zero: the array keeps whatever the
+        // last call on this device left there
+        if (!attn_uses_tile_kernel(mask->kind, unpaired)) {
+            int grid = 0;
+            if ((e = attn_unit_grid(&grid)) != hipSuccess) return device_status(e, "device attribute query");
+            const size_t off = attn_workspace_counter_offset(grid);
+            e = launch_fill_i32(reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + off), 0,
+                                (int64_t)cache->heads * a.n_qtiles, (hipStream_t)stream);
+            if (e != hipSuccess) return device_status(e, "fill kernel");
+        }
+    }
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255)))
         return fail(VDIT_ERR_BUFFER_TOO_SMALL, "workspace %p of %zu bytes; the call needs %zu bytes, 256-byte aligned",
                     workspace, workspace_bytes, ws_need);
     a.workspace = workspace;
     return device_status(launch_attn_fwd(a, (hipStream_t)stream), "attention kernel");
+}
+
+}  // namespace
+
+int vdit_block_attn_fwd(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
+                        const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
+                        float softmax_scale, vdit_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    return attn_fwd_impl(q, rope, q_grid, q_t0, cache, mask, plan_dev, softmax_scale, o, lse, workspace,
+                         workspace_bytes, false, stream);
+}
+
+int vdit_block_attn_fwd_static(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, int32_t q_t0,
+                               const vdit_kv_cache* cache, const vdit_mask_cfg* mask, const int32_t* plan_dev,
+                               float softmax_scale, vdit_tensor o, float* lse, void* stream) {
+    return attn_fwd_impl(q, rope, q_grid, q_t0, cache, mask, plan_dev, softmax_scale, o, lse, nullptr, 0, true,
+                         stream);
 }
 
 int vdit_block_rel_l1_workspace_bytes(int32_t n_blocks, int64_t block_elems, size_t* bytes) {

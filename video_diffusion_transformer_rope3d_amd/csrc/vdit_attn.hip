@@ -24,6 +24,7 @@
 // MFMA is chosen (bits 2 and 3 of the S row index swapped) so that the bf16 P operand is
 // taken from the S accumulator registers as they are and V^T is read from LDS with one
 // 16-byte read per lane.
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1298,6 +1299,35 @@ hipError_t attn_unit_grid(int* grid) {
 size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool order) {
     if (unit_kernel) return kOrderBytes + partial_bytes(grid) + (size_t)heads * n_qtiles * 4;
     return order ? kOrderBytes : 0;
+}
+
+size_t attn_workspace_counter_offset(int grid) { return kOrderBytes + partial_bytes(grid); }
+
+// Scratch of the allocation-free attention entry point: one array per GPU the library runs
+// on, held until the process ends, shared by every call on that GPU.  Host code never uses
+// its name as an address (that is a host-side stand-in): the device address comes from
+// hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) char scratch[kAttnStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t attn_static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 namespace {

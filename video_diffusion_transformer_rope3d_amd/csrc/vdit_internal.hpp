@@ -282,6 +282,11 @@ inline bool attn_uses_tile_kernel(int32_t mask_kind, bool unpaired) { return is_
 // Grid of the unit kernel on the current device, and the workspace a call needs.
 hipError_t attn_unit_grid(int* grid);
 size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool order);
+size_t attn_workspace_counter_offset(int grid);
+// The static scratch of vdit_block_attn_fwd_static: a device array of this many bytes per GPU,
+// and its address on the current device.
+constexpr size_t kAttnStaticScratchBytes = size_t(72) << 20;
+hipError_t attn_static_scratch(void** ptr);
 // Workspace of vdit_plan_dynamic and of vdit_block_rel_l1 (bytes).
 size_t dyn_workspace_bytes(const PlanGeom& g, int32_t n_qtiles, int32_t heads, int32_t head_dim);
 size_t rel_l1_workspace_bytes(int32_t n_blocks, int64_t block_elems);
