@@ -1,6 +1,8 @@
 """GPU-side helpers for the tests: run a workload through libvdit and compare with the oracle."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -29,10 +31,13 @@ def session_for(w, stream=None):
                             long_range_period=m.long_range_period, stream=stream)
 
 
-def run_workload(w, inputs, with_lse=True, rotate_q=True, q_override=None):
-    """History appends, chunk append, device plan, attention.  Returns a dict of results."""
+def run_workload(w, inputs, with_lse=True, rotate_q=True, q_override=None, workspace=None):
+    """History appends, chunk append, device plan, attention.  Returns a dict of results.
+    `workspace`: a binding Workspace for the attention call (the session's own when None)."""
     dt = torch_dtype(w)
     s = session_for(w)
+    if workspace is not None:
+        s.attn_workspace = workspace
     for t0, f, hk, hv in inputs["history"]:
         s.append(to_dev(hk, dt), to_dev(hv, dt), t0)
     s.append(to_dev(inputs["k"], dt), to_dev(inputs["v"], dt), w.q_t0)
@@ -62,11 +67,19 @@ def sample_rows(w, n_random=96, seed=0):
     return np.array(sorted(rows))
 
 
+# Every comparison's achieved margins, by test: (test id, what, max-abs, rel-L2, max-abs bar,
+# rel-L2 bar).  tests/conftest.py prints the worst ones at the end of the run.
+MARGINS = []
+
+
 def compare(o_gpu, o_ref, max_abs=MAX_ABS, rel_l2=REL_L2, what=""):
+    """Element-wise comparison against the bar; returns (max-abs, rel-L2) and records them."""
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite GPU output"
-    err = np.abs(o_gpu - o_ref).max()
-    rel = np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-300)
+    err = float(np.abs(o_gpu - o_ref).max()) if o_gpu.size else 0.0
+    rel = float(np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    MARGINS.append((test, what, err, rel, max_abs, rel_l2))
     assert err <= max_abs and rel <= rel_l2, f"{what}: max-abs {err:.3e} (<= {max_abs}), rel-L2 {rel:.3e} (<= {rel_l2})"
     return err, rel

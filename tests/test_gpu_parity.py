@@ -19,8 +19,9 @@ from harness import compare, device_plan_words, run_workload, sample_rows, sessi
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "tiny_d128", "small_chunk_pad", "small_radial", "small_dense_d64", "wan13b_chunk_h2",
-         "small_stream_radial"]
-LARGE = ["wan13b_chunk", "stream_wrap_straddle", "log_radial", "dense_clip", "stream14b_chunk", "stream_radial_chunk"]
+         "small_stream_radial", "wave_two_chunks"]
+LARGE = ["wan13b_chunk", "stream_wrap_straddle", "log_radial", "dense_clip", "stream14b_chunk", "stream_radial_chunk",
+         "wan13b_chunk_h14"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -371,27 +372,79 @@ def test_deterministic():
 
 
 def test_workspace_reuse_across_shapes_and_streams():
-    """A call with many split tiles leaves partial results in the per-stream workspace; a
-    later call with more (head, query tile) pairs must still find all its per-tile counters
-    at zero and give the oracle's output, on the default stream and on a second stream."""
+    """One caller workspace serves calls of different shapes: a call whose units are all split
+    (2 heads: every unit is merged from partials by counters) leaves its counters at zero, so a
+    later call with more (head, query tile) counters, and one with fewer, both give the
+    oracle's output; the same workspace on a second stream gives the same output."""
     _print("workspace reuse")
-    first = get_workload("wan13b_chunk_h2")
-    run_workload(first, make_inputs(first))
-    w = get_workload("small_radial")
+    ws = B.Workspace()
+    first = get_workload("small_chunk_pad")
+    inp0 = make_inputs(first)
+    r0 = run_workload(first, inp0, workspace=ws)
+    w = get_workload("wan13b_chunk_h2")
     inp = make_inputs(w)
-    r = run_workload(w, inp)
+    r = run_workload(w, inp, workspace=ws)
+    rows = sample_rows(w)
     o = r["o"].float().cpu().numpy()
-    ref = _oracle_rows(w, inp, range(w.heads), np.arange(w.n_q))
+    ref = _oracle_rows(w, inp, range(w.heads), rows)
     for h in range(w.heads):
-        compare(o[:, h], ref[h][0], what=f"after reuse, head {h}")
+        compare(o[rows, h], ref[h][0], what=f"after reuse, head {h}")
+    again = run_workload(first, inp0, workspace=ws)["o"]
+    assert torch.equal(again, r0["o"])
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # the session has no stream of its own: it uses the current one
         o2 = r["session"].attend(r["q"], w.q_frames, w.q_t0, r["plan"])
     torch.cuda.synchronize()
     assert torch.equal(o2, r["o"])
-    again = run_workload(w, inp)["o"]
-    assert torch.equal(again, r["o"])
+
+
+def test_split_stream_path_is_taken():
+    """The 14-head Wan-1.3B geometry takes one round of whole units and a split stream on this
+    device (the schedule model, with the device's own grid); test_attention_parity_sampled checks
+    its outputs, including the last head, whose units are the split ones."""
+    from schedule_model import schedule
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    G = max(8, cus // 8 * 8)
+    sch = schedule([220] * 19, 14, G)
+    if G == 256:
+        assert not sch.whole and sch.rounds == 1 and 0 < sch.sk_base < sch.total
+    split_heads = {h for (h, k) in sch.nseg}
+    assert split_heads and 13 in split_heads or G != 256
+
+
+@pytest.mark.parametrize("name,corrupt", [("small_chunk_pad", "magic"), ("small_chunk_pad", "tiles"),
+                                          ("small_chunk_pad", "span"), ("small_radial", "magic"),
+                                          ("small_radial", "span")])
+def test_rejected_plan_gives_nan_outputs(name, corrupt):
+    """A plan that does not belong to the call (wrong magic, another tile count, a span past the
+    cache) is not computed.  The check is in the kernel, which exits normally, so the call returns
+    OK; the outputs it did not compute are NaN.  A bad header, or a bad span under the unit
+    kernel (every workgroup validates the whole plan), poisons every output; under the tile
+    kernel a bad span poisons its own query tile, here tile 0 of every head."""
+    _print("rejected plan", name, corrupt)
+    w = get_workload(name)
+    inp = make_inputs(w)
+    r = run_workload(w, inp)
+    s = r["session"]
+    bad = r["plan"].clone()
+    nq = int(bad[4].item())
+    if corrupt == "magic":
+        bad[0] = 0
+    elif corrupt == "tiles":
+        bad[4] = nq + 1
+    else:  # the first span of tile 0 starts at the end of the cache (8-aligned, outside it)
+        bad[8 + 3 * nq + 1] = s.cache.kv_rows
+    lse = torch.zeros((w.heads, w.n_q), dtype=torch.float32, device="cuda")
+    o = s.attend(r["q"], w.q_frames, w.q_t0, bad, lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    if corrupt == "span" and w.mask.kind == "log_radial":
+        q0, ql = (int(x) for x in r["plan"][8:10].tolist())
+        assert np.isnan(o[q0:q0 + ql]).all() and np.isnan(lse[:, q0:q0 + ql]).all()
+        assert np.isfinite(o[q0 + ql:]).all()
+    else:
+        assert np.isnan(o).all() and np.isnan(lse).all()
 
 
 def test_query_tile_without_keys():

@@ -403,6 +403,34 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int h, int row, bo
 // Lazy-rescale threshold of the online softmax (log2 units): p = exp2((s - m) c) < 2^kLazy.
 constexpr float kLazy = 8.0f;
 
+// A plan that does not belong to the call (wrong magic or tile count, tiles or spans outside the
+// call or the cache) is not computed: the kernel writes NaN instead, so that the failure shows
+// in the outputs.  poison_rows covers rows [row0, row0 + n) of head h; poison_share covers this
+// workgroup's share (part of parts) of all the call's (token, head) rows.
+template <int D, bool OF32>
+__device__ void poison_row(const AttnArgs& a, int tok, int h, int t) {
+    const int64_t off = (int64_t)tok * a.o_st + (int64_t)h * a.o_sh;
+    for (int d = t * 4; d < D; d += 64 * 4) {
+        if constexpr (OF32) *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off + d) = make_float4(NAN, NAN, NAN, NAN);
+        else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off + d) = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
+    }
+    if (a.lse && t == 0) a.lse[(int64_t)h * a.n_tokens + tok] = NAN;
+}
+
+template <int D, bool OF32>
+__device__ void poison_rows(const AttnArgs& a, int h, int row0, int n) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    for (int r = wave; r < n; r += waves) poison_row<D, OF32>(a, row0 + r, h, lane);
+}
+
+template <int D, bool OF32>
+__device__ void poison_share(const AttnArgs& a, int part, int parts) {
+    const int64_t rows = (int64_t)a.n_tokens * a.heads;
+    const int64_t b = rows * part / parts, e = rows * (part + 1) / parts;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    for (int64_t r = b + wave; r < e; r += waves) poison_row<D, OF32>(a, (int)(r / a.heads), (int)(r % a.heads), lane);
+}
+
 // ---------------------------------------------------------------- tile kernel
 // One workgroup = one (query tile, head), 4 waves, two workgroups per CU; the grid covers
 // all tiles of all heads.  Used where neighbouring query tiles have different span lists
@@ -439,19 +467,28 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
 
     const int32_t* plan = a.plan;
     const int nq = plan[4];
-    // a plan that does not belong to this call is ignored rather than read out of bounds
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles || qt >= nq) return;
+    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles || qt >= nq) {
+        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
+        return;
+    }
     const int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
     const int32_t* row_ptr = qtiles + 2 * nq;
     const int32_t* spans = row_ptr + nq + 1;
     const int q_start = plan_word(qtiles + 2 * qt), q_len = plan_word(qtiles + 2 * qt + 1);
     const int sp_begin = plan_word(row_ptr + qt), sp_end = plan_word(row_ptr + qt + 1);
-    if (q_start < 0 || q_len < 1 || q_len > kBM || q_start + q_len > a.n_tokens || sp_begin < 0 ||
-        sp_begin > sp_end || sp_end > plan[5])
+    if (q_start < 0 || q_len < 1 || q_len > kBM || q_start + q_len > a.n_tokens) {
+        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
         return;
-    for (int sp = sp_begin; sp < sp_end; ++sp) {  // spans must lie inside the cache, 8-aligned
+    }
+    bool bad = sp_begin < 0 || sp_begin > sp_end || sp_end > plan[5];
+    for (int sp = sp_begin; !bad && sp < sp_end; ++sp) {  // spans must lie inside the cache, 8-aligned
         const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
-        if (k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > a.kv_rows) return;
+        bad = k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > a.kv_rows;
+    }
+    if (bad) {
+        poison_rows<D, OF32>(a, h, q_start, q_len);
+        return;
     }
 
     const int r_in = wave * 32 + qi;
@@ -854,8 +891,11 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
 
     const int32_t* plan = a.plan;
     const int nq = a.n_qtiles;
-    // a plan that does not belong to this call is ignored rather than read out of bounds
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[4] != nq || nq > kMaxTiles) return;
+    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[4] != nq || nq > kMaxTiles) {
+        poison_share<D, OF32>(a, blockIdx.x, G);
+        return;
+    }
     const int n_spans = plan[5];
     const int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
     const int32_t* row_ptr = qtiles + 2 * nq;
@@ -892,7 +932,10 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     __syncthreads();
     if (__any(bad) && lane == 0) s_bad = 1;
     __syncthreads();
-    if (uniform(s_bad)) return;
+    if (uniform(s_bad)) {
+        poison_share<D, OF32>(a, blockIdx.x, G);
+        return;
+    }
     if (wave == 0) {
         // run starts (max-scan), unit heads (even offset in the run), partners, unit numbers
         // and the prefix of unit iterations

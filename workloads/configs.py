@@ -202,6 +202,25 @@ _add(Workload(
                              long_range_period=4),
     capacity=7, history=_chunks(4, 13), lowfreq_amp=0.5))
 
+_add(Workload(
+    name="wave_two_chunks", seed=19,
+    description="Two whole 3-frame chunks in one call (frames 12..17, chunks 4 and 5 at different noise levels, "
+                "as in staggered wave denoising): 30x52 tokens per frame, a ring of 9 frames that has wrapped; "
+                "the history wrote chunk 4's frames once already, the call's own append refreshes them with new "
+                "data and adds chunk 5; chunk-causal with 3-frame chunks, so chunk 4 does not see chunk 5; "
+                "2 heads, head_dim 128, data x 1/sqrt(128).",
+    heads=2, head_dim=128, frame_h=30, frame_w=52, q_frames=6, q_t0=12, rope_dims=(44, 42, 42),
+    theta=1e4, mask=MaskSpec("chunk_causal", chunk_frames=3), capacity=9,
+    history=_chunks(3, 15), data_scale=128 ** -0.5))
+
+_add(Workload(
+    name="wan13b_chunk_h14", seed=20,
+    description="Wan-1.3B-shaped chunk with 14 heads: 266 units of one or two query tiles, one round of whole "
+                "units on 256 workgroups, the rest split over all of them.",
+    heads=14, head_dim=128, frame_h=30, frame_w=52, q_frames=3, q_t0=6, rope_dims=(44, 42, 42),
+    theta=1e4, mask=MaskSpec("chunk_causal", chunk_frames=3), capacity=21,
+    history=((0, 3), (3, 3)), data_scale=128 ** -0.5))
+
 WORKLOADS = dict(_W)
 
 
