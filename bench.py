@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--separate-plan", action="store_true",
                     help="static plan from its own launch after the append (default: built in the append launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (by default a run on the Wan-1.3B chunk also times the "
+                         "dense clip, the log-radial clip, the 14B stream and the streaming log-radial chunk)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until reached)")
     ap.add_argument("--qkv", action="store_true",
@@ -72,6 +75,8 @@ def parse():
                     help="also time the stock library call for the same shapes: torch's SDPA (all keys visible "
                          "to every query only) or, with --qkv, the plain bf16 GEMM of F.linear")
     ap.add_argument("--traffic-copy-mib", type=int, default=256)
+    ap.add_argument("--traffic-kernel", default=ATTN_KERNEL, help="kernel name the --traffic counters are taken for")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE, help="where --traffic writes its summary")
     ap.add_argument("--traffic-command", default="")
     return ap.parse_args()
 
@@ -81,15 +86,15 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel source and on this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != source_sha(ATTN_SRC):
+    if t.get("kernel_source_sha256") != source_sha(ATTN_SRC) or t.get("workload", "wan13b_chunk") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -115,9 +120,23 @@ def cpu_baseline(w, inputs, seconds):
         spent += time.perf_counter() - t
         heads += 1
     return dict(value=flop_per_head * heads / spent / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                cpu_model=cpu_model(), affinity_cores=len(os.sched_getaffinity(0)),
                 sample=f"{heads} head passes ({w.heads} heads per chunk), each all {w.n_q} query rows against "
                        f"{len(st.k_phys)} cached keys: RoPE of Q, element mask, fp64 masked softmax attention "
-                       f"({spent:.1f} s); the ring build (K rotation of all heads) is excluded")
+                       f"({spent:.1f} s); the ring build (K rotation of all heads) is excluded; cores = the BLAS "
+                       f"threads the oracle ran on, affinity_cores = the CPUs this process may use")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
 
 
 RAMP_SECONDS = 0.2
@@ -174,8 +193,9 @@ def library_attention(heads, n_q, n_k, head_dim, flop, steps, warmup):
             "ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}
 
 
-def write_traffic(fetch_csv, write_csv, copy_mib, command):
-    """Per-launch HBM bytes of the attention kernel from two rocprofv3 --pmc runs
+def write_traffic(fetch_csv, write_csv, copy_mib, command, kernel=ATTN_KERNEL, workload="wan13b_chunk",
+                  out_file=TRAFFIC_FILE):
+    """Per-launch HBM bytes of an attention kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
     reads for the device-to-device copy of copy_mib MiB made by --calibrate-copy."""
     import csv
@@ -190,8 +210,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
             raise SystemExit(f"no {counter} sample of a kernel matching {needle!r} in {path}")
         return vals
 
-    attn_fetch = per_kernel(fetch_csv, "FETCH_SIZE", ATTN_KERNEL)
-    attn_write = per_kernel(write_csv, "WRITE_SIZE", ATTN_KERNEL)
+    attn_fetch = per_kernel(fetch_csv, "FETCH_SIZE", kernel)
+    attn_write = per_kernel(write_csv, "WRITE_SIZE", kernel)
     # the calibration copy is the largest copy dispatch of the run
     copy_fetch = max(per_kernel(fetch_csv, "FETCH_SIZE", "copyBuffer"))
     copy_write = max(per_kernel(write_csv, "WRITE_SIZE", "copyBuffer"))
@@ -201,14 +221,14 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
     fetch_kib = sum(attn_fetch) / len(attn_fetch)
     write_kib = sum(attn_write) / len(attn_write)
     hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
-    out = {"kernel": ATTN_KERNEL, "kernel_source_sha256": source_sha(ATTN_SRC),
+    out = {"kernel": kernel, "workload": workload, "kernel_source_sha256": source_sha(ATTN_SRC),
            "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
            "dispatches": [len(attn_fetch), len(attn_write)],
            "copy_calibration": {"bytes": copy_bytes, "fetch_kib": copy_fetch, "write_kib": copy_write,
                                 "fetch_factor": f_fetch, "write_factor": f_write},
            "hbm_bytes_per_launch": hbm, "command": command}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    os.makedirs(os.path.dirname(out_file), exist_ok=True)
+    with open(out_file, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -323,27 +343,10 @@ def bench_qkv(args):
     print(json.dumps(result), flush=True)
 
 
-def main():
-    args = parse()
-    if args.qkv:
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
-        bench_qkv(args)
-        return
-    if args.rel_l1:
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
-        bench_rel_l1(args)
-        return
-    if args.traffic:
-        write_traffic(args.traffic[0], args.traffic[1], args.traffic_copy_mib, args.traffic_command)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus})", file=sys.stderr)
-        sys.exit(2)
+def measure(args, name, steps, warmup, cold_steps, tau=None, separate_plan=False, library_reference=False,
+            cpu=False):
+    """One workload's step timed as described in the module docstring: returns the result fields
+    (value, per-launch times, roofline, ...) of its JSON line."""
     import numpy as np
     import torch
 
@@ -351,7 +354,7 @@ def main():
     from video_diffusion_transformer_rope3d_amd import AttentionSession
     from video_diffusion_transformer_rope3d_amd import binding as B
 
-    w = get_workload(args.workload)
+    w = get_workload(name)
     inputs = make_inputs(w)
     dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
 
@@ -367,7 +370,6 @@ def main():
         s.append(dev(hk), dev(hv), t0)
     q, k, v = dev(inputs["q"]), dev(inputs["k"]), dev(inputs["v"])
     o = torch.empty_like(q)
-    tau = args.dynamic_tau
     if tau is None:
         plan = torch.empty(s.plan_bound(w.q_frames, w.q_t0), dtype=torch.int32, device="cuda")
         mask = s.mask
@@ -383,7 +385,7 @@ def main():
         if tau is not None:
             s.append(k, v, w.q_t0)
             s.plan_dynamic(q, w.q_frames, w.q_t0, tau, out=plan)
-        elif args.separate_plan:
+        elif separate_plan:
             s.append(k, v, w.q_t0)
             s.plan(w.q_frames, w.q_t0, out=plan)
         else:
@@ -403,7 +405,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     clock_ramp(step)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     words = plan.cpu().numpy()
@@ -426,43 +428,43 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = t_start.elapsed_time(t_end) / steps
     # per-launch times: K more steps with events around the append (+ plan) and the attention
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     attn_times = [b.elapsed_time(c) for _, b, c in events]
-    attn_avg = sum(attn_times) / args.steps
-    prep_avg = sum(a.elapsed_time(b) for a, b, _ in events) / args.steps
+    attn_avg = sum(attn_times) / steps
+    prep_avg = sum(a.elapsed_time(b) for a, b, _ in events) / steps
     attn_tflops = flop / (attn_avg * 1e-3) / 1e12
 
     # cold: before each step, a 512 MiB write evicts the 256 MB MALL and the L2s, so the step
     # reads its K/V, Q and plan from HBM (the scratch write is outside the timed events)
     cold = []
-    if args.cold_steps > 0:
+    if cold_steps > 0:
         scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.int32, device="cuda")
-        cev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.cold_steps)]
-        for i in range(args.cold_steps):
+        cev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(cold_steps)]
+        for i in range(cold_steps):
             scratch.fill_(i)
             step(cev[i])
         torch.cuda.synchronize()
         cold = [b.elapsed_time(c) for _, b, c in cev]
         del scratch
 
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(w.name)
     result = {
         "metric": METRIC,
         "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "clock_ramp_ms": RAMP_SECONDS * 1e3,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
@@ -476,7 +478,7 @@ def main():
                    "frame": f"{w.frame_h}x{w.frame_w}", "q_t0": w.q_t0, "mask": m.kind,
                    "computed_block_flop": flop,
                    "plan": (f"dynamic tau={tau}" if tau is not None else
-                            "static, separate launch" if args.separate_plan else "static, built in the append launch")},
+                            "static, separate launch" if separate_plan else "static, built in the append launch")},
         "append_plan_ms_per_chunk": round(prep_avg, 4),
         "attn_ms_per_chunk": round(attn_avg, 4),
         "attn_ms_per_chunk_median": round(float(np.median(attn_times)), 4),
@@ -488,15 +490,65 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
-    if args.library_reference:
+    if library_reference:
         n_k = int((s.cache.slot_host >= 0).sum()) * w.tokens_per_frame  # keys of the valid slots
         if n_k and pairs == w.n_q * n_k:
-            result["library_reference"] = library_attention(w.heads, w.n_q, n_k, w.head_dim, flop, args.steps,
-                                                             args.warmup)
+            result["library_reference"] = library_attention(w.heads, w.n_q, n_k, w.head_dim, flop, steps, warmup)
         else:
             result["library_reference"] = None  # masked: no stock call computes the same blocks
-    if not args.no_cpu_baseline:
+    if cpu:
         result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
+    return result
+
+
+# the other workloads one default run also times (the headline is the Wan-1.3B-shaped chunk)
+OTHER_CONFIGS = ("dense_clip", "log_radial", "stream14b_chunk", "stream_radial_chunk")
+
+
+
+
+def main():
+    args = parse()
+    if args.qkv:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_qkv(args)
+        return
+    if args.rel_l1:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_rel_l1(args)
+        return
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.traffic_copy_mib, args.traffic_command,
+                      args.traffic_kernel, args.workload, args.traffic_out)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    result = measure(args, args.workload, args.steps, args.warmup, args.cold_steps, tau=args.dynamic_tau,
+                     separate_plan=args.separate_plan, library_reference=args.library_reference,
+                     cpu=not args.no_cpu_baseline)
+    if not args.no_configs and args.dynamic_tau is None and args.workload == "wan13b_chunk":
+        # every headline workload in the same run, fewer steps each: ms per chunk of the attention
+        # launch (warm, median of cold), its TFLOP/s and fraction of the bf16 peak, the work the
+        # kernel executes per computed-block FLOP, and the append + plan launch
+        result["configs"] = {}
+        for name in OTHER_CONFIGS:
+            r = measure(args, name, min(args.steps, 10), min(args.warmup, 3), min(args.cold_steps, 3))
+            torch.cuda.empty_cache()
+            result["configs"][name] = {
+                "attn_ms_per_chunk": r["attn_ms_per_chunk"], "attn_ms_per_chunk_cold": r["attn_ms_per_chunk_cold"],
+                "attn_tflops": r["attn_tflops"], "attn_frac_of_bf16_peak": r["attn_frac_of_bf16_peak"],
+                "mfma_valid_fraction": r["mfma_valid_fraction"], "append_plan_ms_per_chunk":
+                r["append_plan_ms_per_chunk"], "step_tflops": r["value"], "steps": r["steps"],
+                "kernel": "attn_tile_kernel" if r["config"]["mask"] in ("log_radial", "log_radial_causal")
+                else ATTN_KERNEL, "config": r["config"]}
     print(json.dumps(result), flush=True)
 
 
