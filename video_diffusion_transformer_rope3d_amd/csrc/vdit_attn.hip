@@ -431,133 +431,14 @@ __device__ void poison_share(const AttnArgs& a, int part, int parts) {
     for (int64_t r = b + wave; r < e; r += waves) poison_row<D, OF32>(a, (int)(r / a.heads), (int)(r % a.heads), lane);
 }
 
-// ---------------------------------------------------------------- tile kernel
-// One workgroup = one (query tile, head), 4 waves, two workgroups per CU; the grid covers
-// all tiles of all heads.  Used where neighbouring query tiles have different span lists
-// (log-radial), so that two tiles cannot share one K/V stream.
-//
-// Workgroups are dispatched round-robin over the 8 XCDs; renumber so that each XCD gets a
-// contiguous range of (head, query tile) items, whose K/V then stream through its L2.
+// Tile kernel item numbering: workgroups are dispatched round-robin over the 8 XCDs; renumber
+// so that each XCD gets a contiguous range of (head, query tile) items, whose K/V then stream
+// through its L2.
 __device__ inline int xcd_remap(int bid, int total) {
     constexpr int kXcd = 8;
     int q = total / kXcd, r = total % kXcd;
     int xcd = bid % kXcd, idx = bid / kXcd;
     return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
-template <int D, bool QF32, bool OF32>
-__global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs a) {
-    using T = Tile<D, kTileWaves>;
-    constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int qi = lane & 31, g = lane >> 5;
-    int h, qt;
-    if (a.order) {  // longest tiles first, all heads of a tile together
-        qt = a.order[blockIdx.x / a.heads];
-        h = blockIdx.x % a.heads;
-    } else {
-        const int item = xcd_remap(blockIdx.x, a.n_qtiles * a.heads);
-        h = item / a.n_qtiles;
-        qt = item % a.n_qtiles;
-    }
-
-    const int32_t* plan = a.plan;
-    const int nq = plan[4];
-    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles || qt >= nq) {
-        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
-        return;
-    }
-    const int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
-    const int32_t* row_ptr = qtiles + 2 * nq;
-    const int32_t* spans = row_ptr + nq + 1;
-    const int q_start = plan_word(qtiles + 2 * qt), q_len = plan_word(qtiles + 2 * qt + 1);
-    const int sp_begin = plan_word(row_ptr + qt), sp_end = plan_word(row_ptr + qt + 1);
-    if (q_start < 0 || q_len < 1 || q_len > kBM || q_start + q_len > a.n_tokens) {
-        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
-        return;
-    }
-    bool bad = sp_begin < 0 || sp_begin > sp_end || sp_end > plan[5];
-    for (int sp = sp_begin; !bad && sp < sp_end; ++sp) {  // spans must lie inside the cache, 8-aligned
-        const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
-        bad = k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > a.kv_rows;
-    }
-    if (bad) {
-        poison_rows<D, OF32>(a, h, q_start, q_len);
-        return;
-    }
-
-    const int r_in = wave * 32 + qi;
-    const bool row_valid = r_in < q_len;
-    const int row = q_start + (row_valid ? r_in : q_len - 1);
-    // a wave whose 32 rows all lie past the tile's end (the short last tile of a frame) keeps
-    // its share of the DMA and the barriers but skips the math
-    const bool wave_rows = uniform(wave) * 32 < q_len;
-    bf16x8 qreg[KS];
-    if (wave_rows) load_q_rows<D, QF32>(a, h, row, g, qreg);
-
-    f32x16 oacc[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-    const float c = a.scale_log2;
-    const float lazy_raw = kLazy / c;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    if (sp_begin < sp_end) {
-        int span = sp_begin;
-        int k0 = plan_word(spans + 2 * span), kend = k0 + plan_word(spans + 2 * span + 1);
-        // The words of the span after the current one, loaded when the current one starts with a
-        // vector load (counted by vmcnt, so the tile waits cover it), so that crossing into the
-        // next span does not wait for a plan read before the next tile's DMA is issued.
-        const __amdgpu_buffer_rsrc_t rsp = head_rsrc(spans, (uint32_t)sp_end * 8);
-        u32x2 pf = {0u, 0u};
-        if (span + 1 < sp_end) pf = __builtin_amdgcn_raw_buffer_load_b64(rsp, (uint32_t)(span + 1) * 8, 0, 0);
-        const int wave_u = uniform(wave);
-        const DmaLane<D / 8> kdl = dma_lane<D / 8>(wave_u, lane);
-        const DmaLane<kBN / 8> vdl = dma_lane<kBN / 8>(wave_u, lane);
-        const uint32_t head_bytes = (uint32_t)(a.kv_rows * D * 2);
-        const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.kc + (int64_t)h * a.kv_rows * D, head_bytes);
-        const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.vt + (int64_t)h * D * a.kv_rows, head_bytes);
-        const uint32_t vpitch = (uint32_t)(a.kv_rows * 2);
-        FragLane fl;
-        fl.qi = qi, fl.g = g, fl.krow = swap23(qi);
-        fl.kswz = swz<T::KCH>(fl.krow), fl.vswz = swz<T::VCH>(qi);
-        load_tile_lds<D, kTileWaves>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem);
-        wait_tile_loads();
-        __syncthreads();
-        // (not unrolled by stage as the unit kernel is: measured 2% slower here)
-        int buf = 0;
-        while (true) {
-            int nk0 = k0 + kBN, nkend = kend, nspan = span;
-            if (nk0 >= kend) {
-                ++nspan;
-                if (nspan < sp_end) {
-                    nk0 = uniform((int)pf[0]);
-                    nkend = nk0 + uniform((int)pf[1]);
-                    if (nspan + 1 < sp_end)
-                        pf = __builtin_amdgcn_raw_buffer_load_b64(rsp, (uint32_t)(nspan + 1) * 8, 0, 0);
-                }
-            }
-            const bool has_next = nspan < sp_end;
-            if (has_next)
-                load_tile_lds<D, kTileWaves>(rk, rv, vpitch, nk0, nkend, wave_u, kdl, vdl,
-                                             smem + (buf ^ 1) * T::STAGE);
-            if (wave_rows)
-                tile_step<D, kTileWaves>(smem + buf * T::STAGE, fl, qreg, oacc, m_run, l_run, c, lazy_raw, k0, kend);
-            if (!has_next) break;
-            wait_tile_loads();
-            __syncthreads();
-            buf ^= 1;
-            k0 = nk0;
-            kend = nkend;
-            span = nspan;
-        }
-    }
-    store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, c);
 }
 
 // ---------------------------------------------------------------- tile order
@@ -602,21 +483,23 @@ __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(const int32_t
 }
 
 // ---------------------------------------------------------------- pipelined key loop
-// The unit kernel's key loop is software-pipelined inside each wave: while the softmax of key
-// tile n runs on the VALU, the score MFMAs of tile n + 1 run on the matrix core, then the
-// P.V MFMAs of tile n follow, interleaved with the row sum of tile n and the row max of tile
-// n + 1.  A step therefore reads K of tile n + 1 and V^T of tile n, while the DMA of tile
-// n + 2 is in flight: three LDS stages.  The K tiles of the three stages come first, then
-// the V^T tiles, so every fragment read takes its stage and block as an immediate offset.
-template <int D>
+// The key loops are software-pipelined inside each wave: while the softmax of key tile n runs
+// on the VALU, the score MFMAs of tile n + 1 run on the matrix core, then the P.V MFMAs of
+// tile n follow, interleaved with the row sum of tile n and the row max of tile n + 1.  A step
+// therefore reads K of tile n + 1 and V^T of tile n.  The unit kernel keeps NST = 3 stages of
+// both (the DMA of tile n + 2 in flight); the tile kernel, two workgroups per CU, keeps two K
+// stages and two V^T stages and moves V^T one tile behind K (K of tile n + 2 and V^T of tile
+// n + 1 in flight).  The K tiles of all stages come first, then the V^T tiles, so every
+// fragment read takes its stage and block as an immediate offset.
+template <int D, int NST = 3>
 struct Pipe {
     static constexpr int KS = D / 16;  // k-steps of the score contraction
     static constexpr int DB = D / 32;  // 32-row blocks of O^T
     static constexpr int KCH = D / 8, VCH = kBN / 8;
     static constexpr int KROW = KCH * 16, VROW = VCH * 16;  // LDS bytes per K row / V^T row
     static constexpr int K_BYTES = kBN * KROW, V_BYTES = D * VROW;
-    static constexpr int V_BASE = 3 * K_BYTES;
-    static constexpr int BYTES = 3 * (K_BYTES + V_BYTES);
+    static constexpr int V_BASE = NST * K_BYTES;
+    static constexpr int BYTES = NST * (K_BYTES + V_BYTES);
     static constexpr int NS = 2 * KS;   // score MFMAs per step
     static constexpr int NP = 4 * DB;   // P.V MFMAs per step
     static constexpr int NM = NS + NP;
@@ -633,9 +516,9 @@ struct PipeLane {
     uint32_t v[4];
 };
 
-template <int D>
+template <int D, int NST>
 __device__ inline PipeLane<D> pipe_lane(int qi, int g) {
-    using P = Pipe<D>;
+    using P = Pipe<D, NST>;
     PipeLane<D> pl;
     const int krow = swap23(qi);
     const int kswz = swz<P::KCH>(krow), vswz = swz<P::VCH>(qi);
@@ -652,33 +535,40 @@ __device__ inline PipeLane<D> pipe_lane(int qi, int g) {
     return pl;
 }
 
-// DMA of key tile [k0, k0 + kBN) of a span ending at kend into K stage / V^T stage `st`.
-template <int D, int WAVES>
+// DMA of key tile [k0, k0 + kBN) of a span ending at kend: its K rows into K stage kst, its V^T
+// columns into V^T stage vst (either part skipped when its stage is negative).  In a tail tile,
+// keys at or beyond kend are replaced by in-bounds keys of the span (their scores are masked)
+// and V^T chunks by the last chunk holding a valid key.
+template <int D, int WAVES, int NST>
 __device__ inline void pipe_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t vpitch, int k0,
                                  int kend, int wave, const DmaLane<D / 8>& kl, const DmaLane<kBN / 8>& vl, char* smem,
-                                 int st) {
+                                 int kst, int vst) {
     using T = Tile<D, WAVES>;
-    using P = Pipe<D>;
+    using P = Pipe<D, NST>;
     constexpr int KRPB = 64 / T::KCH, VRPB = 64 / T::VCH;
-    char* kdst = smem + st * P::K_BYTES;
-    char* vdst = smem + P::V_BASE + st * P::V_BYTES;
     const int last = kend - 1 - k0;
+    if (kst >= 0) {
+        char* kdst = smem + kst * P::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < T::K_LOADS; ++i) {
-        const int blk = i * WAVES + wave;
-        const int rowd = min(blk * KRPB + kl.rib, last);
-        const uint32_t voff = (uint32_t)rowd * (D * 2) + kl.chunk * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, voff,
-                                                 (uint32_t)k0 * (D * 2), 0, 0);
+        for (int i = 0; i < T::K_LOADS; ++i) {
+            const int blk = i * WAVES + wave;
+            const int rowd = min(blk * KRPB + kl.rib, last);
+            const uint32_t voff = (uint32_t)rowd * (D * 2) + kl.chunk * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, voff,
+                                                     (uint32_t)k0 * (D * 2), 0, 0);
+        }
     }
-    const int vkey = min(k0 + vl.chunk * 8, (kend - 1) & ~7);
-    const uint32_t vcol = (uint32_t)(vkey - k0) * 2;
+    if (vst >= 0) {
+        char* vdst = smem + P::V_BASE + vst * P::V_BYTES;
+        const int vkey = min(k0 + vl.chunk * 8, (kend - 1) & ~7);
+        const uint32_t vcol = (uint32_t)(vkey - k0) * 2;
 #pragma unroll
-    for (int i = 0; i < T::V_LOADS; ++i) {
-        const int blk = i * WAVES + wave;
-        const uint32_t voff = (uint32_t)vl.rib * vpitch + vcol;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, voff,
-                                                 (uint32_t)(blk * VRPB) * vpitch + (uint32_t)k0 * 2, 0, 0);
+        for (int i = 0; i < T::V_LOADS; ++i) {
+            const int blk = i * WAVES + wave;
+            const uint32_t voff = (uint32_t)vl.rib * vpitch + vcol;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, voff,
+                                                     (uint32_t)(blk * VRPB) * vpitch + (uint32_t)k0 * 2, 0, 0);
+        }
     }
 }
 
@@ -738,10 +628,10 @@ __device__ inline void pipe_first(f32x16 (&s)[2], bool tail, int lim, float& m_r
 }
 
 // Score MFMAs of one tile, not interleaved (the segment's first tile): S^T = K Q^T from K stage st.
-template <int D>
+template <int D, int NST>
 __device__ __forceinline__ void pipe_scores(const char* smem, const PipeLane<D>& pl, int st,
                                             const bf16x8 (&qreg)[D / 16], f32x16 (&sn)[2]) {
-    using P = Pipe<D>;
+    using P = Pipe<D, NST>;
     sn[0] = f32x16{};
     sn[1] = f32x16{};
 #pragma unroll
@@ -773,11 +663,11 @@ __device__ __forceinline__ void pipe_scores(const char* smem, const PipeLane<D>&
 // while it builds block 0 of tile n + 1; so at most three 16-register score blocks are live.
 // Each MFMA with its share of VALU work and its fragment read LOOK MFMAs ahead is one
 // scheduling group, in this order.
-template <int D, int ST, int ST1>
+template <int D, int NST, int ST, int ST1>
 __device__ __forceinline__ void pipe_step(const char* smem, const PipeLane<D>& pl, const bf16x8 (&qreg)[D / 16],
                                           f32x16 (&oacc)[D / 32], const f32x16 (&s)[2], f32x16 (&sn)[2],
                                           const f32x16& negm, float& l_run, float& mt_next) {
-    using P = Pipe<D>;
+    using P = Pipe<D, NST>;
     constexpr int KS = P::KS, DB = P::DB, NM = P::NM, L = P::LOOK;
     constexpr int Q1 = KS, Q2 = Q1 + 2 * DB, Q3 = Q2 + KS;  // quarter boundaries
     auto is_score = [](int i) { return i < Q1 || (i >= Q2 && i < Q3); };
@@ -844,6 +734,144 @@ __device__ __forceinline__ void pipe_step(const char* smem, const PipeLane<D>& p
         sched_fence();
     }
     mt_next = mt;
+}
+
+// ---------------------------------------------------------------- tile kernel
+// One workgroup = one (query tile, head), 4 waves, two workgroups per CU; the grid covers all
+// tiles of all heads.  Used where neighbouring query tiles have different span lists
+// (log-radial, dynamic plans), so that two tiles cannot share one K/V stream.  The key loop is
+// the pipelined one with two K stages and two V^T stages: step n reads K of tile n + 1 and V^T
+// of tile n while K of tile n + 2 and V^T of tile n + 1 are in flight.
+template <int D, bool QF32, bool OF32>
+__global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs a) {
+    using PP = Pipe<D, 2>;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    __shared__ __attribute__((aligned(1024))) char smem[PP::BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int qi = lane & 31, g = lane >> 5;
+    int h, qt;
+    if (a.order) {  // longest tiles first, all heads of a tile together
+        qt = a.order[blockIdx.x / a.heads];
+        h = blockIdx.x % a.heads;
+    } else {
+        const int item = xcd_remap(blockIdx.x, a.n_qtiles * a.heads);
+        h = item / a.n_qtiles;
+        qt = item % a.n_qtiles;
+    }
+
+    const int32_t* plan = a.plan;
+    const int nq = plan[4];
+    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles || qt >= nq) {
+        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
+        return;
+    }
+    const int32_t* qtiles = plan + VDIT_PLAN_HEADER_WORDS;
+    const int32_t* row_ptr = qtiles + 2 * nq;
+    const int32_t* spans = row_ptr + nq + 1;
+    const int q_start = plan_word(qtiles + 2 * qt), q_len = plan_word(qtiles + 2 * qt + 1);
+    const int sp_begin = plan_word(row_ptr + qt), sp_end = plan_word(row_ptr + qt + 1);
+    if (q_start < 0 || q_len < 1 || q_len > kBM || q_start + q_len > a.n_tokens) {
+        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
+        return;
+    }
+    bool bad = sp_begin < 0 || sp_begin > sp_end || sp_end > plan[5];
+    int n_tiles = 0;  // key tiles of the query tile
+    for (int sp = sp_begin; !bad && sp < sp_end; ++sp) {  // spans must lie inside the cache, 8-aligned
+        const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
+        bad = k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > a.kv_rows;
+        n_tiles += (kl + kBN - 1) / kBN;
+    }
+    if (bad) {
+        poison_rows<D, OF32>(a, h, q_start, q_len);
+        return;
+    }
+
+    const int r_in = wave * 32 + qi;
+    const bool row_valid = r_in < q_len;
+    const int row = q_start + (row_valid ? r_in : q_len - 1);
+    // a wave whose 32 rows all lie past the tile's end (the short last tile of a frame) keeps
+    // its share of the DMA and the barriers but skips the math
+    const bool wave_rows = uniform(wave) * 32 < q_len;
+    const float c = a.scale_log2;
+    bf16x8 qreg[KS];
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;  // in log2 units: Q carries the softmax scale and log2(e)
+
+    if (n_tiles > 0) {
+        const int wave_u = uniform(wave);
+        const DmaLane<D / 8> kdl = dma_lane<D / 8>(wave_u, lane);
+        const DmaLane<kBN / 8> vdl = dma_lane<kBN / 8>(wave_u, lane);
+        const uint32_t head_bytes = (uint32_t)(a.kv_rows * D * 2);
+        const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.kc + (int64_t)h * a.kv_rows * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.vt + (int64_t)h * D * a.kv_rows, head_bytes);
+        const uint32_t vpitch = (uint32_t)(a.kv_rows * 2);
+        const PipeLane<D> pl = pipe_lane<D, 2>(qi, g);
+        // key tiles n (k0, kend), n + 1 (k1, kend1), n + 2 (k2, kend2), and the span of the
+        // furthest tile located so far
+        int span = sp_begin;
+        int k0 = plan_word(spans + 2 * span), kend = k0 + plan_word(spans + 2 * span + 1);
+        int k1 = 0, kend1 = 0;
+        auto advance = [&](int k, int ke, int& nk, int& nke) {
+            nk = k + kBN;
+            nke = ke;
+            if (nk >= ke) {
+                ++span;
+                nk = plan_word(spans + 2 * span);
+                nke = nk + plan_word(spans + 2 * span + 1);
+            }
+        };
+        int left = n_tiles - 1;  // tiles after tile n
+        pipe_load<D, kTileWaves, 2>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem, 0, 0);
+        if (left >= 1) {
+            advance(k0, kend, k1, kend1);
+            pipe_load<D, kTileWaves, 2>(rk, rv, vpitch, k1, kend1, wave_u, kdl, vdl, smem, 1, -1);
+        }
+        if (wave_rows) load_q_rows<D, QF32>(a, h, row, g, qreg, c);
+        wait_tile_loads();
+        __syncthreads();
+        f32x16 sacc[2][2];
+        f32x16 negm;
+        if (wave_rows) {
+            pipe_scores<D, 2>(smem, pl, 0, qreg, sacc[0]);
+            pipe_first(sacc[0], k0 + kBN > kend, kend - k0 - g * 8, m_run, negm);
+        }
+        // step n: V^T of tile n in V stage n mod 2, K of tile n + 1 in K stage (n + 1) mod 2
+        auto key_step = [&](auto stc) {  // returns false after the last key tile
+            constexpr int ST = decltype(stc)::value, ST1 = ST ^ 1;
+            wait_tile_loads();
+            __syncthreads();  // K of tile n + 1 and V^T of tile n landed; K stage ST, V^T stage ST1 free
+            int k2 = 0, kend2 = 0;
+            if (left >= 2) {
+                advance(k1, kend1, k2, kend2);
+                pipe_load<D, kTileWaves, 2>(rk, rv, vpitch, k2, kend2, wave_u, kdl, vdl, smem, ST, -1);
+            }
+            if (left >= 1) pipe_load<D, kTileWaves, 2>(rk, rv, vpitch, k1, kend1, wave_u, kdl, vdl, smem, -1, ST1);
+            if (wave_rows) {
+                float mt;
+                pipe_step<D, 2, ST, ST1>(smem, pl, qreg, oacc, sacc[ST], sacc[ST1], negm, l_run, mt);
+                if (left >= 1)
+                    pipe_fixup<D>(sacc[ST1], k1 + kBN > kend1, kend1 - k1 - g * 8, mt, m_run, l_run, oacc, negm);
+            }
+            if (left == 0) return false;
+            --left;
+            k0 = k1;
+            kend = kend1;
+            k1 = k2;
+            kend1 = kend2;
+            return true;
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        while (key_step(I0{}) && key_step(I1{})) {
+        }
+    }
+    store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, 1.0f);
 }
 
 // ---------------------------------------------------------------- unit kernel
@@ -1082,7 +1110,7 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     const DmaLane<kBN / 8> vdl = dma_lane<kBN / 8>(wave_u, lane);
     const uint32_t head_bytes = (uint32_t)(a.kv_rows * D * 2);
     const uint32_t vpitch = (uint32_t)(a.kv_rows * 2);
-    const PipeLane<D> pl = pipe_lane<D>(qi, g);
+    const PipeLane<D> pl = pipe_lane<D, 3>(qi, g);
 
     // Segment order of the stream share.  The unit l segment (from its first iteration) comes
     // first, then the whole units, each started at the iteration index equal to the stream
@@ -1184,10 +1212,10 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                 }
             };
             __syncthreads();  // the previous segment's LDS reads are done
-            pipe_load<D, kUnitWaves>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem, 0);
+            pipe_load<D, kUnitWaves, 3>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem, 0, 0);
             if (left >= 1) {
                 advance(k0, kend, k1, kend1);
-                pipe_load<D, kUnitWaves>(rk, rv, vpitch, k1, kend1, wave_u, kdl, vdl, smem, 1);
+                pipe_load<D, kUnitWaves, 3>(rk, rv, vpitch, k1, kend1, wave_u, kdl, vdl, smem, 1, 1);
             }
             // Q loads overlap the first K/V tiles; Q carries the softmax scale and log2(e)
             if (active) load_q_rows<D, QF32>(a, h, row, g, qreg, c);
@@ -1196,7 +1224,7 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
             f32x16 sacc[2][2];
             f32x16 negm;
             if (active) {
-                pipe_scores<D>(smem, pl, 0, qreg, sacc[0]);
+                pipe_scores<D, 3>(smem, pl, 0, qreg, sacc[0]);
                 pipe_first(sacc[0], k0 + kBN > kend, kend - k0 - g * 8, m_run, negm);
             }
             // Step n: tile n's V^T is in stage n mod 3 and tile n + 1's K in the next stage; the
@@ -1212,11 +1240,11 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                 int k2 = 0, kend2 = 0;
                 if (left >= 2) {
                     advance(k1, kend1, k2, kend2);
-                    pipe_load<D, kUnitWaves>(rk, rv, vpitch, k2, kend2, wave_u, kdl, vdl, smem, ST2);
+                    pipe_load<D, kUnitWaves, 3>(rk, rv, vpitch, k2, kend2, wave_u, kdl, vdl, smem, ST2, ST2);
                 }
                 if (active) {
                     float mt;
-                    pipe_step<D, ST, ST1>(smem, pl, qreg, oacc, sacc[SB], sacc[SB ^ 1], negm, l_run, mt);
+                    pipe_step<D, 3, ST, ST1>(smem, pl, qreg, oacc, sacc[SB], sacc[SB ^ 1], negm, l_run, mt);
                     if (left >= 1)
                         pipe_fixup<D>(sacc[SB ^ 1], k1 + kBN > kend1, kend1 - k1 - g * 8, mt, m_run, l_run, oacc, negm);
                 }
