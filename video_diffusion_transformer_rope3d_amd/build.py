@@ -65,6 +65,50 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers: the host code of every source (argument validation, the host plan
+# builder, RoPE tables, launch set-up) is built with AddressSanitizer and UndefinedBehaviour-
+# Sanitizer; the device code is built as usual.  The library links the shared sanitizer
+# runtime, which a process that loads it must preload (sanitizer_runtime()).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for pat in (os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"),
+                os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"),
+                "/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"):
+        hits = sorted(glob.glob(pat))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("the shared AddressSanitizer runtime of hipcc's clang was not found")
+
+
+def build_sanitized(out_dir: str, jobs: int = 4) -> str:
+    """libvdit.so with sanitized host code, built under out_dir; returns its path."""
+    cc = hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        r = subprocess.run([cc, *flags(), *SANITIZE, "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    lib = os.path.join(out_dir, "libvdit.so")
+    r = subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-Xarch_host", "-fsanitize=address",
+                        "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", lib],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)

@@ -10,9 +10,10 @@
 // smallest candidate proxies of the query tile.  The kept tiles become maximal runs of
 // physical key indices in the usual plan words.
 //
-// Five launches: pooled queries [nq][H*D], pooled keys transposed [H*D][nk], the proxies
-// [nq][nk] (a small fp32 product), then per query tile the threshold and the run count,
-// and per query tile its offset (a sum over the counts before it) and its runs.
+// Four launches: one that pools the queries [nq][H*D] and the keys (transposed, [H*D][nk])
+// side by side, the partial proxies [nq][nk] (a small fp32 product, its channels split over
+// slices), then per query tile the proxies summed, the threshold and the run count, and per
+// query tile its offset (a sum over the counts before it) and its runs.
 #include <algorithm>
 #include <utility>
 
