@@ -278,14 +278,17 @@ int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vd
  * bf16 rounding.  A query tile's keys may be split over several workgroups, whose partial
  * results are merged in a fixed order: outputs are deterministic for a given device.
  * workspace: device scratch of at least vdit_block_attn_workspace_bytes(mask, q_grid, q_t0,
- *   cache) bytes, asked on the device that runs the call (the size depends on its CU count;
- *   0 for static log-radial plans, which need none).  For CHUNK_CAUSAL and DENSE plans it
- *   holds per-tile arrival counters (4 bytes per head and query tile), which must be zero
- *   before the workspace's first use and which every call leaves zero, and partial results
- *   (two 135 KB slots per CU); for dynamic plans, the order of the query tiles.  The caller
- *   zeroes a new workspace once (all bytes) and may pass it to any later call on the same
- *   device whose size query does not exceed its size; every region sits at an offset that
- *   depends on the device only.  Calls that may run at the same time need separate workspaces.
+ *   cache) bytes, asked on the device that runs the call (0 for static log-radial plans,
+ *   which need none).  CHUNK_CAUSAL and DENSE plans: partial results (two 135 KB slots per
+ *   CU, so the size depends on the device's CU count) and, above them and above every
+ *   dynamic-plan layout, per-tile arrival counters (4 bytes per head and query tile), which
+ *   must be zero before the workspace's first use and which every call leaves zero.  Dynamic
+ *   plans (host arithmetic: 256 + align256((n_qtiles + 1024 / heads) * 32) + 4096 +
+ *   1024 * 67584 bytes, about 69 MB): the call's work list (query tiles with many kept keys
+ *   are cut into chunks of near-equal length, listed longest first) and the chunks' partial
+ *   results, all rewritten by every call.  The caller zeroes a new workspace once (all bytes)
+ *   and may pass it to any later call on the same device whose size query does not exceed
+ *   its size.  Calls that may run at the same time need separate workspaces.
  * Errors: head counts or head_dim differing from the cache's, head_dim not 64 or 128 ->
  * INVALID_ARG / UNSUPPORTED; more than 4096 query tiles in one call -> UNSUPPORTED (split the
  * call by frames); workspace NULL or below the size query -> BUFFER_TOO_SMALL. */

@@ -1,4 +1,6 @@
-"""A host model of the unit attention kernel's work schedule (test infrastructure).
+"""Host models of the attention kernels' work schedules (test infrastructure).
+
+Unit kernel (static CHUNK_CAUSAL and DENSE plans):
 
 It replays, in plain Python, how each of the G workgroups of the unit kernel picks its work
 from a plan: query tiles with equal span lists paired into units, rounds of whole units, then
@@ -9,6 +11,12 @@ the share's elapsed iteration count and wrapped), the segment of its first unit.
 are merged by the last of their segments to arrive; the model counts those segments the way
 the kernel does.  Tests use it to check that every key iteration of every unit is computed
 exactly once, and to know which path a geometry takes on a device with a given CU count.
+
+Tile kernel on a dynamic plan (`tile_work_list`): each query tile's key steps n_t, the chunk
+length L = max(8, ceil(W / 512)) with W = heads * sum(n_t), tiles with n_t > L cut into
+ceil(n_t / L) chunks of near-equal length (the first n_t mod c one step longer), each chunk of
+a split tile with its partial-result slot (split tiles numbered in tile order); the list is
+ordered longest first.  The GPU tests compare the device's list with it.
 """
 from __future__ import annotations
 
@@ -138,3 +146,47 @@ def cover_counts(sch, unit_iters, heads):
             for i in range(a, b):
                 cnt[(h, k, i)] = cnt.get((h, k, i), 0) + 1
     return cnt, segs
+
+
+TILE_SLOTS = 512       # balancing target: tile workgroups resident at once
+SPLIT_CAP = 2 * TILE_SLOTS
+SPLIT_MIN = 8
+
+
+def tile_steps_from_plan(qtiles, row_ptr, spans):
+    """Key steps (KBN keys each) of every query tile of a plan."""
+    return [sum((int(kl) + KBN - 1) // KBN for _, kl in spans[row_ptr[q]:row_ptr[q + 1]]) for q in range(len(qtiles))]
+
+
+def tile_work_list(steps, heads):
+    """(items, chunk length) of the tile kernel's work list: items are (tile, begin, end,
+    slot, chunk, chunks) in the device's order up to ties (equal lengths in any order; lengths
+    of 1023 steps and more count as equal)."""
+    W = heads * sum(steps)
+    L = max(SPLIT_MIN, -(-W // TILE_SLOTS))
+    chunks = [-(-n // L) if n > L else 1 for n in steps]
+    if sum(c for c in chunks if c > 1) * heads > SPLIT_CAP:  # the kernel's guard; never taken
+        chunks = [1] * len(steps)
+    items, first = [], 0
+    for t, (n, c) in enumerate(zip(steps, chunks)):
+        beg = 0
+        for k in range(c):
+            ln = n // c + (1 if k < n % c else 0)
+            items.append((t, beg, beg + ln, first + k if c > 1 else -1, k, c))
+            beg += ln
+        if c > 1:
+            first += c
+    items.sort(key=lambda it: -min(it[2] - it[1], 1023))
+    return items, L
+
+
+def item_start(row_ptr, spans, tile, begin):
+    """(span, skip): the plan span that holds key step `begin` of `tile`, and the steps before
+    it inside that span."""
+    left = begin
+    for sp in range(row_ptr[tile], row_ptr[tile + 1]):
+        n = (int(spans[sp][1]) + KBN - 1) // KBN
+        if left < n:
+            return sp, left
+        left -= n
+    return row_ptr[tile], 0  # an empty item

@@ -272,23 +272,26 @@ def test_workspace_size_queries_and_short_workspaces(L):
     radial = B.mask_cfg("log_radial")
     assert L.vdit_block_attn_workspace_bytes(ctypes.byref(radial), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
     assert n.value == 0
-    # dynamic plans: the order of the query tiles (4096 words)
+    # dynamic plans: item count, work list (the call's 3 query tiles plus at most 1024 / heads
+    # chunks, 32 bytes each), 1024 arrival counters and 1024 partial slots of 4 waves x
+    # (64 lanes x 64 floats of O + 64 (max, sum) pairs)
+    a256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
     dyn_m = B.dynamic_mask(B.mask_cfg("chunk_causal", 1))
     assert L.vdit_block_attn_workspace_bytes(ctypes.byref(dyn_m), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
-    assert n.value == 4096 * 4
+    dyn_need = 256 + a256((3 + 1024 // 2) * 32) + 4096 + 1024 * 4 * (64 * 64 + 2 * 64) * 4
+    assert n.value == dyn_need == 256 + a256((3 + 1024 // 2) * 32) + 4096 + 1024 * 67584
     assert L.vdit_block_attn_workspace_bytes(ctypes.byref(dyn_m), g, 0, ctypes.byref(desc), None) == \
         B.VDIT_ERR_INVALID_ARG
     assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(dyn_m), fake, 0.0, t, None, None,
                                  0, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
     assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(dyn_m), fake, 0.0, t, None, fake,
-                                 4096 * 4 - 1, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
+                                 dyn_need - 1, None) == B.VDIT_ERR_BUFFER_TOO_SMALL
     assert L.vdit_block_attn_fwd(t, None, g, 0, ctypes.byref(desc), ctypes.byref(dyn_m), fake, 0.0, t, None,
-                                 fake + 16, 1 << 20, None) == B.VDIT_ERR_BUFFER_TOO_SMALL  # not 256-byte aligned
+                                 fake + 16, 1 << 27, None) == B.VDIT_ERR_BUFFER_TOO_SMALL  # not 256-byte aligned
     # dynamic plan: pooled queries and keys, partial and final proxies, run and pair counts
     m = B.mask_cfg("chunk_causal", 1)
     assert L.vdit_plan_dynamic_workspace_bytes(ctypes.byref(m), g, 0, ctypes.byref(desc), ctypes.byref(n)) == 0
     nq, nk, hd = 3, 3, 2 * 64
-    a256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert n.value == (a256(nq * hd * 4) + a256(hd * nk * 4) + a256(nq * nk * 4 * 1) + a256(nq * nk * 4) +
                        a256(nq * 4) + a256(nq * 8))
     words = ctypes.c_size_t(0)

@@ -26,6 +26,7 @@ from workloads.synth import bf16_round
 from video_diffusion_transformer_rope3d_amd import binding as B
 
 from harness import compare, device_plan_words, run_workload
+from schedule_model import item_start, tile_steps_from_plan, tile_work_list
 
 pytestmark = pytest.mark.gpu
 
@@ -157,3 +158,16 @@ def test_attention_on_a_dynamic_plan(name, tau):
         ref, ref_lse = oracle.masked_attention(q_rot[:, h], st.k[:, h], st.v[:, h], allowed, w.head_dim ** -0.5)
         compare(o_gpu[:, h], ref, what=f"{name} tau {tau} head {h}")
         np.testing.assert_allclose(lse.cpu().numpy()[h], ref_lse, atol=1e-2, rtol=0)
+    # the work list the call ran: the host model's, up to the order of equal lengths
+    want, _ = tile_work_list(tile_steps_from_plan(qt.tolist(), rp.tolist(), sp.tolist()), w.heads)
+    ws = s.attn_workspace.buf.cpu().numpy()
+    n_items = int(ws[:4].view(np.int32)[0])
+    raw = ws[256:256 + 32 * n_items].view(np.int32).reshape(-1, 8)
+    got = [tuple(x) for x in raw[:, :6].tolist()]
+    assert sorted(got) == sorted(want)
+    rpl, spl = rp.tolist(), sp.tolist()
+    for it in raw.tolist():  # each item's first key step located in the plan's spans
+        assert tuple(it[6:]) == item_start(rpl, spl, it[0], it[1])
+    assert [min(it[2] - it[1], 1023) for it in got] == [min(it[2] - it[1], 1023) for it in want]
+    if name == "wan13b_chunk_h2":  # long tiles: chunks and their merge are exercised
+        assert any(it[5] > 1 for it in got)

@@ -7,6 +7,7 @@ import pytest
 
 import oracle
 from workloads import get_workload, make_inputs
+import schedule_model as sched
 from schedule_model import cover_counts, schedule, units_from_plan
 
 
@@ -57,3 +58,38 @@ def test_plan_units_of_the_gpu_workloads(name, heads):
     assert h == heads
     assert [u[2] for u in units] == [220] * 19
     assert [u[1] for u in units] == [True] * 18 + [False]
+
+
+@pytest.mark.parametrize("heads", [1, 2, 12, 40])
+def test_tile_work_list_covers_each_tile_once_within_the_bounds(heads):
+    """Chunks of a tile cover its key steps once, in order, with lengths at most L that differ by at
+    most one; split chunks of all heads stay below the partial-slot cap and the list below
+    n_qtiles + 1024 / heads items (the bounds the workspace size rests on); the list is longest
+    first."""
+    rng = np.random.default_rng(heads)
+    for trial in range(200):
+        nq = int(rng.integers(1, 400))
+        kind = trial % 4
+        if kind == 0:
+            steps = rng.integers(0, 600, nq)
+        elif kind == 1:  # a few very long tiles among short ones
+            steps = np.where(rng.random(nq) < 0.05, rng.integers(300, 5000, nq), rng.integers(0, 20, nq))
+        elif kind == 2:
+            steps = rng.integers(0, 9, nq)
+        else:
+            steps = np.full(nq, int(rng.integers(1, 2000)))
+        steps = [int(x) for x in steps]
+        items, L = sched.tile_work_list(steps, heads)
+        assert len(items) <= nq + sched.SPLIT_CAP // heads
+        split = [it for it in items if it[3] >= 0]
+        assert len(split) * heads < sched.SPLIT_CAP
+        assert sorted({it[3] for it in split}) == list(range(len(split)))
+        for t in range(nq):
+            mine = sorted((it for it in items if it[0] == t), key=lambda it: it[4])
+            assert [it[4] for it in mine] == list(range(len(mine)))
+            assert mine[0][1] == 0 and mine[-1][2] == steps[t]
+            assert all(a[2] == b[1] for a, b in zip(mine, mine[1:]))
+            lens = [it[2] - it[1] for it in mine]
+            assert max(lens) - min(lens) <= 1 and (len(mine) == 1 or max(lens) <= L)
+        lens = [min(it[2] - it[1], 1023) for it in items]
+        assert lens == sorted(lens, reverse=True)

@@ -24,6 +24,7 @@
 // MFMA is chosen (bits 2 and 3 of the S row index swapped) so that the bf16 P operand is
 // taken from the S accumulator registers as they are and V^T is read from LDS with one
 // 16-byte read per lane.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -44,6 +45,24 @@ constexpr int kBN = 64;   // keys per iteration
 constexpr int kMaxTiles = kAttnMaxQTiles;  // query tiles per call (the unit table lives in LDS)
 constexpr int kTableBytes = (2 * (kMaxTiles + 1) * 4 + 255) / 256 * 256;
 
+// Work item of the tile kernel on a dynamic plan: key steps [begin, end) of query tile `tile`,
+// the first of them `skip` steps into plan span `span`; slot >= 0 for chunk `chunk` of a tile
+// split into `chunks` (its partial-result slot, per head), -1 for a whole tile; chunks < 0 for
+// a tile whose spans the schedule rejected.
+struct TileItem {
+    int32_t tile, begin, end, slot, chunk, chunks, span, skip;
+};
+static_assert(sizeof(TileItem) == 32, "two 16-byte loads per item");
+// Balancing target of the dynamic-plan schedule: tile workgroups resident at once (two per CU
+// on 256 CUs).  Split chunks of all heads stay below kSplitCap; no chunk is cut below about
+// kSplitMin key steps.
+constexpr int kTileSlots = 512;
+constexpr int kSplitCap = 2 * kTileSlots;
+constexpr int kSplitMin = 8;
+__host__ __device__ constexpr int32_t tile_items_max(int32_t n_qtiles, int32_t heads) {
+    return n_qtiles + kSplitCap / heads;
+}
+
 struct AttnArgs {
     const void* q;
     int64_t q_st, q_sh;
@@ -60,7 +79,9 @@ struct AttnArgs {
     float scale_log2;
     int32_t* cnt;  // per-tile arrival counters, zero between calls
     float* part;   // partial results, two slots per workgroup
-    const int32_t* order;  // tile kernel: query tiles longest first (NULL: plan order)
+    // tile kernel on a dynamic plan: the work list (NULL: one item per tile and head, plan order)
+    const TileItem* items;
+    const int32_t* n_items;
 };
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -258,6 +279,62 @@ __device__ __forceinline__ void load_q_rows(const AttnArgs& a, int h, int row, i
     }
 }
 
+// The same rows in two phases, for a kernel that starts one query tile per workgroup: issue()
+// sends the row loads and every table load at once, finish() rotates, scales and packs.  The
+// tile DMA is issued in between, so the rotation runs while the K/V tiles are in flight and
+// the loads of the rows never wait behind it.
+template <int D, bool QF32>
+struct QRows {
+    static constexpr int KS = D / 16, PER = QF32 ? 2 : 1;
+    using Raw = std::conditional_t<QF32, float4, u32x4>;
+    Raw raw[KS][PER];
+    float2 cs[KS][4];
+
+    __device__ __forceinline__ void issue(const AttnArgs& a, int h, int row, int g) {
+        const int f = row / a.hw, s = row % a.hw;
+        const int pt = a.t0 + f, ph = s / a.wf, pw = s % a.wf;
+        const int64_t qoff = (int64_t)row * a.q_st + (int64_t)h * a.q_sh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = ks * 16 + g * 8;
+            if constexpr (QF32) {
+                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff + d0);
+                raw[ks][0] = p[0];
+                raw[ks][1] = p[1];
+            } else {
+                raw[ks][0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qoff + d0);
+            }
+        }
+        if (a.has_rope) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs[ks][e] = rope_cs(a.rope, ks * 8 + g * 4 + e, pt, ph, pw);
+        }
+    }
+
+    __device__ __forceinline__ void finish(const AttnArgs& a, bf16x8 (&qreg)[KS], float qscale) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[8];
+            if constexpr (QF32) {
+                const float4 u = raw[ks][0], v = raw[ks][1];
+                x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+                x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+            } else {
+                unpack_bf16x8(raw[ks][0], x);
+            }
+            if (a.has_rope) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rope_apply(cs[ks][e], x[2 * e], x[2 * e + 1]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= qscale;
+            qreg[ks] = __builtin_bit_cast(bf16x8, pack_bf16x8(x));
+        }
+    }
+};
+
 // Lane-level fragment addressing of one wave inside a stage.
 struct FragLane {
     int qi, g;   // query row of the lane inside the wave's 32, half-wave
@@ -441,45 +518,259 @@ __device__ inline int xcd_remap(int bid, int total) {
     return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-// ---------------------------------------------------------------- tile order
-// Query tiles of a dynamic-threshold plan carry very different numbers of keys.  Workgroups
-// start in grid order, so the tile kernel takes its (tile, head) items longest first (list
-// scheduling: the long ones do not end up in the last wave of workgroups).  One workgroup
-// sums each tile's span lengths (a wave per tile) and ranks the tiles by (count, lower tile
-// first): a tile's rank is the number of tiles ahead of it, read from LDS by every thread in
-// step (broadcast reads, no barriers).  A plan that does not belong to the call gives the
-// plan order; the tile kernel rejects its items itself.
-constexpr int kOrderThreads = 1024;
-__global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(const int32_t* plan, int32_t nq, int32_t* order) {
-    __shared__ int32_t s_rp[kMaxTiles + 1];
-    __shared__ int32_t s_cnt[kMaxTiles];
-    const int tid = threadIdx.x;
+// ---------------------------------------------------------------- partial results
+// A workgroup that computes part of a (query tile, head)'s keys leaves a partial result: per
+// wave the O^T accumulators of its 64 lanes (DB * 16 floats each, stored float4-interleaved
+// over lanes) and the lanes' (max, sum), all relative to the lane's own exponent base.
+// Partials are written and read with device-scope (sc1) accesses, which go to the point of
+// coherence of all XCDs, so the per-XCD L2s need no write-back or invalidation; each wave waits
+// for its stores to complete before the workgroup counts in.
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer builtins: device scope (sc1)
+
+template <int D, int WAVES = kUnitWaves>
+struct Partial {
+    static constexpr int DB = D / 32;
+    static constexpr int O_FLOATS = DB * 16 * 64;
+    static constexpr int WAVE = O_FLOATS + 2 * 64;
+    static constexpr int SLOT = WAVES * WAVE;
+};
+
+// This wave's partial at byte offset pw (the wave's base) of rpart.
+template <int D>
+__device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rpart, uint32_t pw, int lane,
+                                              const f32x16 (&oacc)[D / 32], float m, float l) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 v = {__float_as_uint(oacc[db][4 * j]), __float_as_uint(oacc[db][4 * j + 1]),
+                             __float_as_uint(oacc[db][4 * j + 2]), __float_as_uint(oacc[db][4 * j + 3])};
+            // the block's constant offset goes to the scalar offset, so the lane needs one
+            // address register for all sixteen stores
+            __builtin_amdgcn_raw_buffer_store_b128(v, rpart, pw + lane * 16, (db * 4 + j) * 1024, kSc1);
+        }
+    const u32x2 ml = {__float_as_uint(m), __float_as_uint(l)};
+    __builtin_amdgcn_raw_buffer_store_b64(ml, rpart, pw + Partial<D>::O_FLOATS * 4 + lane * 8, 0, kSc1);
+}
+
+// Folds the wave's partial at byte offset pu into (oacc, M, L): all three start empty
+// (zeros, -inf, 0) before the first fold.
+template <int D>
+__device__ __forceinline__ void partial_fold(__amdgpu_buffer_rsrc_t rpart, uint32_t pu, int lane,
+                                             f32x16 (&oacc)[D / 32], float& M, float& L) {
+    const u32x2 mlu = __builtin_amdgcn_raw_buffer_load_b64(rpart, pu + Partial<D>::O_FLOATS * 4 + lane * 8, 0, kSc1);
+    const float mu = __uint_as_float(mlu[0]), lu = __uint_as_float(mlu[1]);
+    const float mn = fmaxf(M, mu);
+    const float a1 = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+    const float a2 = mu == -INFINITY ? 0.f : fast_exp2(mu - mn);
+    // one 32-row block at a time (a bound on the loads in flight)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 vu = __builtin_amdgcn_raw_buffer_load_b128(rpart, pu + lane * 16, (db * 4 + j) * 1024, kSc1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[db][4 * j + e] = oacc[db][4 * j + e] * a1 + __uint_as_float(vu[e]) * a2;
+        }
+        sched_fence();
+    }
+    L = L * a1 + lu * a2;
+    M = mn;
+}
+
+// ---------------------------------------------------------------- dynamic-plan schedule
+// Query tiles of a dynamic-threshold plan carry very different numbers of keys, and with one
+// workgroup per (tile, head) the longest tiles alone would set the kernel's duration.  One
+// workgroup ahead of the attention kernel lists the work:
+//  * n_t = key steps (kBN keys each) of tile t, W = heads * (sum of n_t), and the chunk length
+//    L = max(kSplitMin, ceil(W / kTileSlots)), kTileSlots being the tile workgroups the target
+//    device holds at once (two per CU on 256 CUs);
+//  * a tile with n_t > L becomes c_t = ceil(n_t / L) chunks whose lengths differ by at most one
+//    step.  Each chunk leaves its partial result (unnormalised O, row max, row sum) in the
+//    workspace; the last chunk of a (tile, head) to arrive folds them in chunk order, so the
+//    result does not depend on which chunk finishes last;
+//  * the items (whole tiles and chunks) are listed longest first (buckets of one step; lengths
+//    from kLenBuckets - 1 on share a bucket), so the workgroups that start last run short items.
+// A split tile has c_t < n_t / L + 1 < 2 n_t / L chunks, so the split chunks of all heads number
+// fewer than 2 W / L <= 2 kTileSlots = kSplitCap: the partial slots, the arrival counters and
+// the item list have bounds that need no knowledge of the plan.  The counters are zeroed here,
+// on the stream of the attention kernel that uses them.  A plan that does not belong to the
+// call gives one item per tile (the tile kernel then rejects the plan itself).
+constexpr int kSchedThreads = 1024;
+constexpr int kLenBuckets = 1024;
+static_assert(kLenBuckets == kSchedThreads, "one histogram bucket per thread in the scan");
+
+// Block-wide exclusive prefix sum of one value per thread (every thread calls it); *total gets
+// the sum of all values.  tmp holds kSchedThreads / 64 + 1 words.
+__device__ int sched_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < kSchedThreads / 64; ++w) {
+            const int t = tmp[w];
+            tmp[w] = run;
+            run += t;
+        }
+        tmp[kSchedThreads / 64] = run;
+    }
+    __syncthreads();
+    const int r = tmp[wave] + x - v;
+    *total = tmp[kSchedThreads / 64];
+    __syncthreads();  // tmp may be reused by the next call
+    return r;
+}
+
+// Block-wide sum of one 64-bit value per thread, returned to every thread.
+__device__ int64_t sched_sum64(int64_t v, int64_t* tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) tmp[wave] = v;
+    __syncthreads();
+    int64_t r = 0;
+    for (int w = 0; w < kSchedThreads / 64; ++w) r += tmp[w];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void tile_schedule_kernel(const int32_t* plan, int32_t nq, int32_t heads,
+                                                                      int64_t kv_rows, TileItem* items,
+                                                                      int32_t* n_items, int32_t* cnt) {
+    constexpr int PER = (kMaxTiles + kSchedThreads - 1) / kSchedThreads;  // tiles per thread in scans
+    constexpr int NW = kSchedThreads / 64;
+    __shared__ int32_t s_n[kMaxTiles];     // key steps of tile t; -1: its spans are rejected
+    __shared__ int32_t s_f[kMaxTiles];     // first split slot of tile t
+    __shared__ int32_t s_cur[kLenBuckets];
+    __shared__ int32_t s_span[kSplitCap];  // per split slot: the chunk's first span and its skip
+    __shared__ int32_t s_skip[kSplitCap];
+    __shared__ int32_t s_tmp[NW + 1];
+    __shared__ int64_t s_tmp64[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool ok = plan[0] == (int32_t)VDIT_PLAN_MAGIC && plan[4] == nq && nq <= kMaxTiles;
     const int n_spans = ok ? plan[5] : 0;
     const int32_t* row_ptr = plan + VDIT_PLAN_HEADER_WORDS + 2 * nq;
     const int32_t* spans = row_ptr + nq + 1;
-    for (int t = tid; t <= nq; t += kOrderThreads) s_rp[t] = ok ? row_ptr[t] : 0;
-    __syncthreads();
-    // one wave per tile: lanes stride over the tile's spans, a shuffle tree adds them
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int t = wave; t < nq; t += kOrderThreads / 64) {
-        const int b = max(s_rp[t], 0), e = min(s_rp[t + 1], n_spans);
-        int n = 0;
-        for (int sp = b + lane; sp < e; sp += 64) n += max(spans[2 * sp + 1], 0);
+    // Key steps per tile, a wave per tile, and the checks the tile kernel would make: the span
+    // list inside the plan, every span non-empty, 8-aligned and inside the cache.
+    for (int t = wave; t < nq; t += NW) {
+        int64_t n = 0;
+        bool bad = !ok;
+        if (ok) {
+            const int b = row_ptr[t], e = row_ptr[t + 1];
+            bad = b < 0 || b > e || e > n_spans;
+            if (!bad) {
+                bool lane_bad = false;
+                for (int sp = b + lane; sp < e; sp += 64) {
+                    const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
+                    lane_bad |= k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > kv_rows;
+                    n += ((int64_t)max(kl, 0) + kBN - 1) / kBN;
+                }
+                bad = __any(lane_bad);
+            }
+        }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
-        if (lane == 0) s_cnt[t] = n;
+        if (lane == 0) s_n[t] = bad ? -1 : (int32_t)min(n, (int64_t)1 << 24);
     }
     __syncthreads();
-    for (int t = tid; t < nq; t += kOrderThreads) {
-        const unsigned c = (unsigned)s_cnt[t];
-        int rank = 0;
-        for (int u = 0; u < nq; ++u) {
-            const unsigned cu = (unsigned)s_cnt[u];
-            rank += cu > c || (cu == c && u < t);
-        }
-        order[rank] = t;
+    // W (64-bit: a tile has at most 2^24 steps) and the chunk length
+    int64_t mine = 0;
+    for (int t = tid; t < nq; t += kSchedThreads) mine += max(s_n[t], 0);
+    const int64_t W = sched_sum64(mine, s_tmp64) * heads;
+    int64_t L = max((int64_t)kSplitMin, (W + kTileSlots - 1) / kTileSlots);
+    auto chunks = [&](int n) { return (int64_t)n > L ? (int)(((int64_t)n + L - 1) / L) : 1; };
+    // first split slot of each tile: prefix over tiles of c_t (split tiles only), in tile order
+    int loc[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int t = tid * PER + i;
+        const int c = t < nq ? chunks(s_n[t]) : 1;
+        loc[i] = c > 1 ? c : 0;
+        sum += loc[i];
     }
+    int n_split = 0;
+    int pre = sched_scan(sum, s_tmp, &n_split);
+    if ((int64_t)n_split * heads > kSplitCap) {  // cannot happen (see above); then split nothing
+        L = INT64_MAX / 2;
+        n_split = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) loc[i] = 0;
+        pre = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int t = tid * PER + i;
+        if (t < nq) s_f[t] = pre;
+        pre += loc[i];
+    }
+    s_cur[tid] = 0;
+    __syncthreads();
+    // First span of every chunk after the first of a split tile, a wave per split tile: the
+    // lanes take 64 spans at a time with their step prefix; chunk k starts at step
+    // k * (n / c) + min(k, n % c).
+    for (int t = wave; t < nq; t += NW) {
+        const int n = s_n[t], c = chunks(n);
+        if (c == 1) continue;
+        const int b = row_ptr[t], e = row_ptr[t + 1];
+        int base = 0;  // steps of the spans before this batch
+        for (int sp0 = b; sp0 < e; sp0 += 64) {
+            const int sp = sp0 + lane;
+            const int st = sp < e ? (spans[2 * sp + 1] + kBN - 1) / kBN : 0;
+            int incl = st;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            const int lo = base + incl - st, hi = base + incl;
+            for (int k = 1; k < c; ++k) {
+                const int bk = k * (n / c) + min(k, n % c);
+                if (lo <= bk && bk < hi) {
+                    s_span[s_f[t] + k] = sp;
+                    s_skip[s_f[t] + k] = bk - lo;
+                }
+            }
+            base += __shfl(incl, 63);
+        }
+    }
+    // items per length bucket (longest first), their start positions, then the items
+    auto bucket = [](int len) { return kLenBuckets - 1 - min(len, kLenBuckets - 1); };
+    for (int t = tid; t < nq; t += kSchedThreads) {
+        const int n = max(s_n[t], 0), c = chunks(n);
+        for (int k = 0; k < c; ++k) atomicAdd(&s_cur[bucket(n / c + (k < n % c))], 1);
+    }
+    __syncthreads();
+    int count = 0;
+    const int start = sched_scan(s_cur[tid], s_tmp, &count);
+    s_cur[tid] = start;
+    __syncthreads();
+    for (int t = tid; t < nq; t += kSchedThreads) {
+        const int n = s_n[t];
+        if (n < 0) {
+            items[atomicAdd(&s_cur[bucket(0)], 1)] = TileItem{t, 0, 0, -1, 0, -1, 0, 0};
+            continue;
+        }
+        const int c = chunks(n), b = ok ? row_ptr[t] : 0;
+        int beg = 0;
+        for (int k = 0; k < c; ++k) {
+            const int len = n / c + (k < n % c);
+            const int pos = atomicAdd(&s_cur[bucket(len)], 1);
+            const int span = k == 0 ? b : s_span[s_f[t] + k], skip = k == 0 ? 0 : s_skip[s_f[t] + k];
+            items[pos] = TileItem{t, beg, beg + len, c > 1 ? s_f[t] + k : -1, k, c, span, skip};
+            beg += len;
+        }
+    }
+    if (tid == 0) *n_items = count;
+    for (int i = tid; i < kSplitCap; i += kSchedThreads) cnt[i] = 0;
 }
 
 // ---------------------------------------------------------------- pipelined key loop
@@ -747,25 +1038,43 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
     using PP = Pipe<D, 2>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) char smem[PP::BYTES];
+    // one LDS object (see the unit kernel): the stages, then the arrival word of split items
+    __shared__ __attribute__((aligned(1024))) char smem[PP::BYTES + 64];
+    int& s_arrived = *reinterpret_cast<int*>(smem + PP::BYTES);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, g = lane >> 5;
-    int h, qt;
-    if (a.order) {  // longest tiles first, all heads of a tile together
-        qt = a.order[blockIdx.x / a.heads];
+
+    const int32_t* plan = a.plan;
+    const int nq = plan[4];
+    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles) {
+        poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
+        return;
+    }
+    // the work item: whole tile (begin 0, end -1: all its key steps) or chunk of a split tile
+    int h, qt, it_begin = 0, it_end = -1, it_slot = -1, it_chunk = 0, it_chunks = 1, it_span = 0, it_skip = 0;
+    if (a.items) {  // the list is longest first, all heads of an item together
+        const int it = blockIdx.x / a.heads;
         h = blockIdx.x % a.heads;
+        if (it >= uniform(*a.n_items)) return;
+        const int4 w0 = reinterpret_cast<const int4*>(a.items + it)[0];
+        const int4 w1 = reinterpret_cast<const int4*>(a.items + it)[1];
+        qt = uniform(w0.x);
+        it_begin = uniform(w0.y);
+        it_end = uniform(w0.z);
+        it_slot = uniform(w0.w);
+        it_chunk = uniform(w1.x);
+        it_chunks = uniform(w1.y);
+        it_span = uniform(w1.z);
+        it_skip = uniform(w1.w);
     } else {
         const int item = xcd_remap(blockIdx.x, a.n_qtiles * a.heads);
         h = item / a.n_qtiles;
         qt = item % a.n_qtiles;
     }
-
-    const int32_t* plan = a.plan;
-    const int nq = plan[4];
-    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles || qt >= nq) {
+    if (qt < 0 || qt >= nq) {
         poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
         return;
     }
@@ -773,17 +1082,29 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
     const int32_t* row_ptr = qtiles + 2 * nq;
     const int32_t* spans = row_ptr + nq + 1;
     const int q_start = plan_word(qtiles + 2 * qt), q_len = plan_word(qtiles + 2 * qt + 1);
-    const int sp_begin = plan_word(row_ptr + qt), sp_end = plan_word(row_ptr + qt + 1);
     if (q_start < 0 || q_len < 1 || q_len > kBM || q_start + q_len > a.n_tokens) {
         poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
         return;
     }
-    bool bad = sp_begin < 0 || sp_begin > sp_end || sp_end > plan[5];
-    int n_tiles = 0;  // key tiles of the query tile
-    for (int sp = sp_begin; !bad && sp < sp_end; ++sp) {  // spans must lie inside the cache, 8-aligned
-        const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
-        bad = k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > a.kv_rows;
-        n_tiles += (kl + kBN - 1) / kBN;
+    bool bad;
+    if (a.items) {
+        // the schedule kernel has checked the tile's spans (the same rules as below; chunks < 0:
+        // rejected) and located the item's first key step; the slot range is checked here
+        bad = it_chunks < 0 || it_begin < 0 || it_begin > it_end ||
+              (it_end > it_begin && (it_span < 0 || it_span >= plan[5] || it_skip < 0)) ||
+              (it_slot >= 0 && (it_chunk < 0 || it_chunk >= it_chunks || it_slot < it_chunk ||
+                                (int64_t)(it_slot - it_chunk + it_chunks) * a.heads > kSplitCap));
+    } else {
+        const int sp_begin = plan_word(row_ptr + qt), sp_end = plan_word(row_ptr + qt + 1);
+        bad = sp_begin < 0 || sp_begin > sp_end || sp_end > plan[5];
+        int n_tiles = 0;  // key tiles of the query tile
+        for (int sp = sp_begin; !bad && sp < sp_end; ++sp) {  // spans must lie inside the cache, 8-aligned
+            const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
+            bad = k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > a.kv_rows;
+            n_tiles += (kl + kBN - 1) / kBN;
+        }
+        it_end = n_tiles;
+        it_span = sp_begin;
     }
     if (bad) {
         poison_rows<D, OF32>(a, h, q_start, q_len);
@@ -803,7 +1124,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;  // in log2 units: Q carries the softmax scale and log2(e)
 
-    if (n_tiles > 0) {
+    if (it_end > it_begin) {
         const int wave_u = uniform(wave);
         const DmaLane<D / 8> kdl = dma_lane<D / 8>(wave_u, lane);
         const DmaLane<kBN / 8> vdl = dma_lane<kBN / 8>(wave_u, lane);
@@ -813,9 +1134,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
         const uint32_t vpitch = (uint32_t)(a.kv_rows * 2);
         const PipeLane<D> pl = pipe_lane<D, 2>(qi, g);
         // key tiles n (k0, kend), n + 1 (k1, kend1), n + 2 (k2, kend2), and the span of the
-        // furthest tile located so far
-        int span = sp_begin;
-        int k0 = plan_word(spans + 2 * span), kend = k0 + plan_word(spans + 2 * span + 1);
+        // furthest tile located so far; the item starts it_skip steps into span it_span
+        int span = it_span;
+        const int span_k0 = plan_word(spans + 2 * span);
+        int k0 = span_k0 + it_skip * kBN, kend = span_k0 + plan_word(spans + 2 * span + 1);
         int k1 = 0, kend1 = 0;
         auto advance = [&](int k, int ke, int& nk, int& nke) {
             nk = k + kBN;
@@ -826,13 +1148,15 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
                 nke = nk + plan_word(spans + 2 * span + 1);
             }
         };
-        int left = n_tiles - 1;  // tiles after tile n
+        int left = it_end - it_begin - 1;  // tiles after tile n
+        QRows<D, QF32> qr;
+        if (wave_rows) qr.issue(a, h, row, g);
         pipe_load<D, kTileWaves, 2>(rk, rv, vpitch, k0, kend, wave_u, kdl, vdl, smem, 0, 0);
         if (left >= 1) {
             advance(k0, kend, k1, kend1);
             pipe_load<D, kTileWaves, 2>(rk, rv, vpitch, k1, kend1, wave_u, kdl, vdl, smem, 1, -1);
         }
-        if (wave_rows) load_q_rows<D, QF32>(a, h, row, g, qreg, c);
+        if (wave_rows) qr.finish(a, qreg, c);
         wait_tile_loads();
         __syncthreads();
         f32x16 sacc[2][2];
@@ -871,22 +1195,34 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
         while (key_step(I0{}) && key_step(I1{})) {
         }
     }
-    store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, 1.0f);
+    if (it_slot < 0) {
+        store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, 1.0f);
+        return;
+    }
+    // chunk of a split tile: leave the partial in its slot, count in; the last chunk of the
+    // (tile, head) to arrive folds all of them in chunk order
+    using TP = Partial<D, kTileWaves>;
+    using TP128 = Partial<128, kTileWaves>;  // slots are sized for head_dim 128
+    const __amdgpu_buffer_rsrc_t rpart = head_rsrc(a.part, (uint32_t)((size_t)kSplitCap * TP128::SLOT * 4));
+    const int first = it_slot - it_chunk;  // slot of chunk 0
+    if (wave_rows)
+        partial_store<D>(rpart, (uint32_t)(((it_slot * a.heads + h) * TP128::SLOT + wave * TP::WAVE) * 4), lane,
+                         oacc, m_run, l_run);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) s_arrived = atomicAdd(a.cnt + (first * a.heads + h), 1);
+    __syncthreads();
+    if (uniform(s_arrived) != it_chunks - 1 || !wave_rows) return;
+    float M = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    for (int k = 0; k < it_chunks; ++k)
+        partial_fold<D>(rpart, (uint32_t)((((first + k) * a.heads + h) * TP128::SLOT + wave * TP::WAVE) * 4), lane,
+                        oacc, M, L);
+    store_rows<D, OF32>(a, h, row, row_valid, g, oacc, M, L, 1.0f);
 }
 
 // ---------------------------------------------------------------- unit kernel
-constexpr int kSc1 = 16;  // cache-policy operand of the buffer builtins: device scope (sc1)
-
-// Floats of one workgroup's partial result: per wave the O^T accumulators of its 64 lanes
-// (DB * 16 floats each, stored float4-interleaved over lanes) and the lanes' (max, sum).
-template <int D>
-struct Partial {
-    static constexpr int DB = D / 32;
-    static constexpr int O_FLOATS = DB * 16 * 64;
-    static constexpr int WAVE = O_FLOATS + 2 * 64;
-    static constexpr int SLOT = kUnitWaves * WAVE;
-};
-
 template <int D, bool QF32, bool OF32>
 __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs a) {
     constexpr int kThreads = kUnitWaves * 64;
@@ -1267,27 +1603,9 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                 if (active) store_rows<D, OF32>(a, h, row, row_valid, g, oacc, m_run, l_run, 1.0f);
             } else {
                 // Split unit: leave the partial in this workgroup's slot (0: the first unit of
-                // its share, 1: the last), then count in.  Partials are written and read with
-                // device-scope (sc1) accesses, which go to the point of coherence of all XCDs, so
-                // the per-XCD L2s need no write-back or invalidation; each wave waits for its
-                // stores to complete before the workgroup counts in.
+                // its share, 1: the last), then count in.
                 const uint32_t pw = (uint32_t)(((2 * w + slot) * P::SLOT + wave * P::WAVE) * 4);
-                if (active) {
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const u32x4 v = {__float_as_uint(oacc[db][4 * j]), __float_as_uint(oacc[db][4 * j + 1]),
-                                             __float_as_uint(oacc[db][4 * j + 2]),
-                                             __float_as_uint(oacc[db][4 * j + 3])};
-                            // the block's constant offset goes to the scalar offset, so the lane
-                            // needs one address register for all sixteen stores
-                            __builtin_amdgcn_raw_buffer_store_b128(v, rpart, pw + lane * 16, (db * 4 + j) * 1024,
-                                                                   kSc1);
-                        }
-                    const u32x2 ml = {__float_as_uint(m_run), __float_as_uint(l_run)};
-                    __builtin_amdgcn_raw_buffer_store_b64(ml, rpart, pw + P::O_FLOATS * 4 + lane * 8, 0, kSc1);
-                }
+                if (active) partial_store<D>(rpart, pw, lane, oacc, m_run, l_run);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 int32_t* counter = a.cnt + (h * n_units + k);
@@ -1312,13 +1630,14 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
                             const long long ub = wg_begin(u);
                             if (wg_begin(u + 1) == ub) continue;
                             const uint32_t pu = (uint32_t)(((2 * u + (ub >= ut ? 0 : 1)) * P::SLOT + wave * P::WAVE) * 4);
+                            // partial_fold written out: as a call, the register allocator spills
+                            // inside the key loop
                             const u32x2 mlu =
                                 __builtin_amdgcn_raw_buffer_load_b64(rpart, pu + P::O_FLOATS * 4 + lane * 8, 0, kSc1);
                             const float mu = __uint_as_float(mlu[0]), lu = __uint_as_float(mlu[1]);
                             const float mn = fmaxf(M, mu);
                             const float a1 = M == -INFINITY ? 0.f : fast_exp2(M - mn);
                             const float a2 = mu == -INFINITY ? 0.f : fast_exp2(mu - mn);
-                            // one 32-row block at a time (a bound on the loads in flight)
 #pragma unroll
                             for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -1344,15 +1663,32 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     }
 }
 
-// Workspace layout (caller-owned, see vdit_block_attn_workspace_bytes): the tile order of
-// dynamic plans (kMaxTiles words), then the split-unit partials (two slots per workgroup, sized
-// for head_dim 128 whatever the call's), then the per-tile arrival counters.  Every region
-// starts at an offset that depends on the device only, so a word that served as a counter is
-// never reused as anything else and stays zero between calls (the last arriver of a tile resets
-// its counter); the caller zeroes the workspace once.
-constexpr size_t kOrderBytes = (size_t)kMaxTiles * 4;
+// Workspace layouts (caller-owned, see vdit_block_attn_workspace_bytes), every region 256-byte
+// aligned.  Tile kernel on a dynamic plan: the item count, the item list, the arrival counters
+// and the partial slots of split tiles; the schedule kernel writes all of them before the
+// attention kernel reads any, so their contents between calls do not matter.  Unit kernel: the
+// split-unit partials (two slots per workgroup, sized for head_dim 128 whatever the call's) from
+// offset 0, then the per-tile arrival counters, above the largest dynamic-plan layout as well.
+// A counter word is thus never used as anything else, by either kernel, and stays zero between
+// calls (the last arriver of a tile resets it): the caller zeroes the workspace once.
+constexpr size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct TileWs {
+    size_t items, cnt, part, bytes;
+};
+constexpr TileWs tile_ws(int32_t n_qtiles, int32_t heads) {
+    TileWs w{};
+    w.items = 256;
+    w.cnt = w.items + align256((size_t)tile_items_max(n_qtiles, heads) * sizeof(TileItem));
+    w.part = w.cnt + align256((size_t)kSplitCap * 4);
+    w.bytes = w.part + (size_t)kSplitCap * Partial<128, kTileWaves>::SLOT * 4;
+    return w;
+}
 
 size_t partial_bytes(int grid) { return (size_t)2 * grid * Partial<128>::SLOT * 4; }
+
+// the largest dynamic-plan layout (kMaxTiles query tiles, one head)
+constexpr size_t kTileWsMax = tile_ws(kMaxTiles, 1).bytes;
 
 }  // namespace
 
@@ -1367,12 +1703,12 @@ hipError_t attn_unit_grid(int* grid) {
     return hipSuccess;
 }
 
-size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool order) {
-    if (unit_kernel) return kOrderBytes + partial_bytes(grid) + (size_t)heads * n_qtiles * 4;
-    return order ? kOrderBytes : 0;
+size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool split) {
+    if (unit_kernel) return attn_workspace_counter_offset(grid) + (size_t)heads * n_qtiles * 4;
+    return split ? tile_ws(n_qtiles, heads).bytes : 0;
 }
 
-size_t attn_workspace_counter_offset(int grid) { return kOrderBytes + partial_bytes(grid); }
+size_t attn_workspace_counter_offset(int grid) { return std::max(partial_bytes(grid), kTileWsMax); }
 
 // Scratch of the allocation-free attention entry point: one array per GPU the library runs
 // on, held until the process ends, shared by every call on that GPU.  Host code never uses
@@ -1408,20 +1744,28 @@ hipError_t launch_unit(AttnArgs a, char* ws, hipStream_t s) {
     int grid = 0;
     hipError_t e = attn_unit_grid(&grid);
     if (e != hipSuccess) return e;
-    a.part = reinterpret_cast<float*>(ws + kOrderBytes);
-    a.cnt = reinterpret_cast<int32_t*>(ws + kOrderBytes + partial_bytes(grid));
+    a.part = reinterpret_cast<float*>(ws);
+    a.cnt = reinterpret_cast<int32_t*>(ws + attn_workspace_counter_offset(grid));
     attn_unit_kernel<D, QF, OF><<<grid, kUnitWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
 
 template <int D, bool QF, bool OF>
-hipError_t launch_tile(AttnArgs a, bool longest_first, char* ws, hipStream_t s) {
-    const unsigned blocks = (unsigned)(a.n_qtiles * a.heads);
-    a.order = nullptr;
-    if (longest_first) {
-        int32_t* order = reinterpret_cast<int32_t*>(ws);
-        tile_order_kernel<<<1, kOrderThreads, 0, s>>>(a.plan, a.n_qtiles, order);
-        a.order = order;
+hipError_t launch_tile(AttnArgs a, bool split, char* ws, hipStream_t s) {
+    unsigned blocks = (unsigned)(a.n_qtiles * a.heads);
+    a.items = nullptr;
+    a.n_items = nullptr;
+    if (split) {  // dynamic plan: the work list first, on the same stream
+        const TileWs w = tile_ws(a.n_qtiles, a.heads);
+        int32_t* n_items = reinterpret_cast<int32_t*>(ws);
+        TileItem* items = reinterpret_cast<TileItem*>(ws + w.items);
+        a.cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+        a.part = reinterpret_cast<float*>(ws + w.part);
+        tile_schedule_kernel<<<1, kSchedThreads, 0, s>>>(a.plan, a.n_qtiles, a.heads, a.kv_rows, items, n_items,
+                                                         a.cnt);
+        a.items = items;
+        a.n_items = n_items;
+        blocks = (unsigned)(tile_items_max(a.n_qtiles, a.heads) * a.heads);
     }
     attn_tile_kernel<D, QF, OF><<<blocks, kTileWaves * 64, 0, s>>>(a);
     return hipGetLastError();

@@ -44,14 +44,30 @@ __device__ inline void unpack_bf16x8(u32x4 u, float x[8]) {
 // "Timeripple ...", Metodologia 1, channel groups per axis).
 // (cos, sin) of channel pair p at position (t, h, w): the pair's axis table, row = the
 // position on that axis.  Branch-free (selects), so that the loads of several pairs can be
-// issued together.
+// issued together.  The tables' addresses and row lengths are first read into scalar
+// registers (every kernel passes one RopeDev to all its lanes): left as a choice between
+// fields of the struct, the compiler loads the chosen field per lane, one dependent global
+// load ahead of every table read.
+typedef __attribute__((address_space(1))) const float rope_gfloat;  // global memory
+__device__ inline rope_gfloat* rope_uniform_ptr(const float2* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<rope_gfloat*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ inline float2 rope_cs(const RopeDev& r, int32_t p, int32_t t, int32_t h, int32_t w) {
-    const bool in_t = p < r.pairs_t, in_h = p < r.pairs_t + r.pairs_h;
-    const float2* tab = in_t ? r.tab_t : (in_h ? r.tab_h : r.tab_w);
+    const int32_t nt = __builtin_amdgcn_readfirstlane(r.pairs_t), nh = __builtin_amdgcn_readfirstlane(r.pairs_h);
+    const int32_t nw = __builtin_amdgcn_readfirstlane(r.pairs_w);
+    rope_gfloat* tt = rope_uniform_ptr(r.tab_t);
+    rope_gfloat* th = rope_uniform_ptr(r.tab_h);
+    rope_gfloat* tw = rope_uniform_ptr(r.tab_w);
+    const bool in_t = p < nt, in_h = p < nt + nh;
+    rope_gfloat* tab = in_t ? tt : (in_h ? th : tw);
     const int32_t coord = in_t ? t : (in_h ? h : w);
-    const int32_t pitch = in_t ? r.pairs_t : (in_h ? r.pairs_h : r.pairs_w);
-    const int32_t col = in_t ? p : (in_h ? p - r.pairs_t : p - r.pairs_t - r.pairs_h);
-    return tab[(int64_t)coord * pitch + col];
+    const int32_t pitch = in_t ? nt : (in_h ? nh : nw);
+    const int32_t col = in_t ? p : (in_h ? p - nt : p - nt - nh);
+    rope_gfloat* e = tab + 2 * ((int64_t)coord * pitch + col);
+    return make_float2(e[0], e[1]);
 }
 
 __device__ inline void rope_apply(float2 cs, float& x0, float& x1) {

@@ -281,7 +281,7 @@ hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t s);
 inline bool attn_uses_tile_kernel(int32_t mask_kind, bool unpaired) { return is_radial(mask_kind) || unpaired; }
 // Grid of the unit kernel on the current device, and the workspace a call needs.
 hipError_t attn_unit_grid(int* grid);
-size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool order);
+size_t attn_workspace_bytes(int grid, int32_t heads, int32_t n_qtiles, bool unit_kernel, bool split);
 size_t attn_workspace_counter_offset(int grid);
 // The static scratch of vdit_block_attn_fwd_static: a device array of this many bytes per GPU,
 // and its address on the current device.
