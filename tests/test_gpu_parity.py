@@ -413,16 +413,18 @@ def test_split_stream_path_is_taken():
     assert split_heads and 13 in split_heads or G != 256
 
 
-@pytest.mark.parametrize("name,corrupt", [("small_chunk_pad", "magic"), ("small_chunk_pad", "tiles"),
-                                          ("small_chunk_pad", "span"), ("small_radial", "magic"),
-                                          ("small_radial", "span")])
-def test_rejected_plan_gives_nan_outputs(name, corrupt):
+@pytest.mark.parametrize("name,corrupt,dyn", [("small_chunk_pad", "magic", False), ("small_chunk_pad", "tiles", False),
+                                              ("small_chunk_pad", "span", False), ("small_radial", "magic", False),
+                                              ("small_radial", "span", False), ("small_chunk_pad", "magic", True),
+                                              ("small_chunk_pad", "span", True)])
+def test_rejected_plan_gives_nan_outputs(name, corrupt, dyn):
     """A plan that does not belong to the call (wrong magic, another tile count, a span past the
     cache) is not computed.  The check is in the kernel, which exits normally, so the call returns
     OK; the outputs it did not compute are NaN.  A bad header, or a bad span under the unit
     kernel (every workgroup validates the whole plan), poisons every output; under the tile
-    kernel a bad span poisons its own query tile, here tile 0 of every head."""
-    _print("rejected plan", name, corrupt)
+    kernel a bad span poisons its own query tile, here tile 0 of every head.  With the dynamic
+    flag (the tile kernel behind its schedule kernel, which checks the spans) the same holds."""
+    _print("rejected plan", name, corrupt, "dynamic" if dyn else "")
     w = get_workload(name)
     inp = make_inputs(w)
     r = run_workload(w, inp)
@@ -436,10 +438,10 @@ def test_rejected_plan_gives_nan_outputs(name, corrupt):
     else:  # the first span of tile 0 starts at the end of the cache (8-aligned, outside it)
         bad[8 + 3 * nq + 1] = s.cache.kv_rows
     lse = torch.zeros((w.heads, w.n_q), dtype=torch.float32, device="cuda")
-    o = s.attend(r["q"], w.q_frames, w.q_t0, bad, lse=lse)
+    o = s.attend(r["q"], w.q_frames, w.q_t0, bad, lse=lse, mask=B.dynamic_mask(s.mask) if dyn else None)
     torch.cuda.synchronize()
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
-    if corrupt == "span" and w.mask.kind == "log_radial":
+    if corrupt == "span" and (w.mask.kind == "log_radial" or dyn):
         q0, ql = (int(x) for x in r["plan"][8:10].tolist())
         assert np.isnan(o[q0:q0 + ql]).all() and np.isnan(lse[:, q0:q0 + ql]).all()
         assert np.isfinite(o[q0 + ql:]).all()
@@ -447,10 +449,12 @@ def test_rejected_plan_gives_nan_outputs(name, corrupt):
         assert np.isnan(o).all() and np.isnan(lse).all()
 
 
-def test_query_tile_without_keys():
+@pytest.mark.parametrize("dyn", [False, True])
+def test_query_tile_without_keys(dyn):
     """A plan row with no spans (possible in a hand-made plan) gives O = 0 and LSE = -inf
-    for that query tile; every other tile is unchanged."""
-    _print("query tile without keys")
+    for that query tile; every other tile is unchanged (with the dynamic flag: as the same
+    kernels compute them on the full plan)."""
+    _print("query tile without keys", "dynamic" if dyn else "")
     w = get_workload("small_chunk_pad")
     inp = make_inputs(w)
     r = run_workload(w, inp)
@@ -467,13 +471,19 @@ def test_query_tile_without_keys():
     hdr[5] = len(keep)
     words = np.concatenate([hdr, qt.ravel(), rp2, sp[keep].ravel()]).astype(np.int32)
     plan2 = torch.from_numpy(words).to("cuda")
+    mask = B.dynamic_mask(r["session"].mask) if dyn else None
     lse = torch.empty((w.heads, w.n_q), dtype=torch.float32, device="cuda")
-    o = r["session"].attend(r["q"], w.q_frames, w.q_t0, plan2, lse=lse)
+    o = r["session"].attend(r["q"], w.q_frames, w.q_t0, plan2, lse=lse, mask=mask)
+    if dyn:
+        ref_lse = torch.empty_like(lse)
+        ref_o = r["session"].attend(r["q"], w.q_frames, w.q_t0, r["plan"], lse=ref_lse, mask=mask)
+    else:
+        ref_o, ref_lse = r["o"], r["lse"]
     torch.cuda.synchronize()
     rows = slice(int(qt[drop, 0]), int(qt[drop, 0] + qt[drop, 1]))
     assert (o[rows].float() == 0).all()
     assert torch.isneginf(lse[:, rows]).all()
     other = torch.ones(w.n_q, dtype=torch.bool, device="cuda")
     other[rows] = False
-    assert torch.equal(o[other], r["o"][other])
-    assert torch.equal(lse[:, other], r["lse"][:, other])
+    assert torch.equal(o[other], ref_o[other])
+    assert torch.equal(lse[:, other], ref_lse[:, other])

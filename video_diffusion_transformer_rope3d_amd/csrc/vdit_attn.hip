@@ -646,8 +646,11 @@ __global__ __launch_bounds__(kSchedThreads) void tile_schedule_kernel(const int3
                                                                       int32_t* n_items, int32_t* cnt) {
     constexpr int PER = (kMaxTiles + kSchedThreads - 1) / kSchedThreads;  // tiles per thread in scans
     constexpr int NW = kSchedThreads / 64;
+    __shared__ int32_t s_rp[kMaxTiles + 1];     // the plan's row pointers
+    __shared__ unsigned long long s_n64[kMaxTiles];
     __shared__ int32_t s_n[kMaxTiles];     // key steps of tile t; -1: its spans are rejected
-    __shared__ int32_t s_f[kMaxTiles];     // first split slot of tile t
+    __shared__ int32_t s_f[kMaxTiles];     // a rejected span of tile t, then its first split slot
+    __shared__ int32_t s_rows_ok;
     __shared__ int32_t s_cur[kLenBuckets];
     __shared__ int32_t s_span[kSplitCap];  // per split slot: the chunk's first span and its skip
     __shared__ int32_t s_skip[kSplitCap];
@@ -658,28 +661,61 @@ __global__ __launch_bounds__(kSchedThreads) void tile_schedule_kernel(const int3
     const int n_spans = ok ? plan[5] : 0;
     const int32_t* row_ptr = plan + VDIT_PLAN_HEADER_WORDS + 2 * nq;
     const int32_t* spans = row_ptr + nq + 1;
-    // Key steps per tile, a wave per tile, and the checks the tile kernel would make: the span
-    // list inside the plan, every span non-empty, 8-aligned and inside the cache.
-    for (int t = wave; t < nq; t += NW) {
-        int64_t n = 0;
-        bool bad = !ok;
-        if (ok) {
-            const int b = row_ptr[t], e = row_ptr[t + 1];
-            bad = b < 0 || b > e || e > n_spans;
-            if (!bad) {
-                bool lane_bad = false;
-                for (int sp = b + lane; sp < e; sp += 64) {
-                    const int k0 = spans[2 * sp], kl = spans[2 * sp + 1];
-                    lane_bad |= k0 < 0 || (k0 & 7) || kl < 1 || (int64_t)k0 + kl > kv_rows;
-                    n += ((int64_t)max(kl, 0) + kBN - 1) / kBN;
+    // Key steps per tile, and the checks the tile kernel would make: row pointers that rise
+    // inside the span list (else every tile is rejected), every span non-empty, 8-aligned and
+    // inside the cache.  The spans are cut into one contiguous run per thread, read eight at a
+    // time; a run's tile is found by binary search in the row pointers and followed from there.
+    for (int t = tid; t <= nq; t += kSchedThreads) s_rp[t] = ok ? row_ptr[t] : 0;
+    for (int t = tid; t < nq; t += kSchedThreads) {
+        s_n64[t] = 0;
+        s_f[t] = 0;
+    }
+    if (tid == 0) s_rows_ok = ok ? 1 : 0;
+    __syncthreads();
+    for (int t = tid; t < nq; t += kSchedThreads)
+        if (s_rp[t] < 0 || s_rp[t] > s_rp[t + 1] || s_rp[t + 1] > n_spans) s_rows_ok = 0;
+    __syncthreads();
+    const bool rows_ok = s_rows_ok != 0;
+    if (rows_ok) {
+        const int lo = s_rp[0], hi = s_rp[nq];
+        const int per = (hi - lo + kSchedThreads - 1) / kSchedThreads;
+        const int first = lo + tid * per, end = min(first + per, hi);
+        int t = 0;  // last tile with s_rp[t] <= first
+        for (int step = 1 << 12; step > 0; step >>= 1)
+            if (t + step <= nq && s_rp[t + step] <= first) t += step;
+        unsigned long long acc = 0;
+        bool bad = false;
+        auto flush = [&]() {
+            if (acc) atomicAdd(&s_n64[t], acc);
+            if (bad) s_f[t] = 1;
+            acc = 0;
+            bad = false;
+        };
+        for (int base = first; base < end; base += 8) {
+            int k0[8], kl[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (base + j < end) {
+                    k0[j] = spans[2 * (base + j)];
+                    kl[j] = spans[2 * (base + j) + 1];
                 }
-                bad = __any(lane_bad);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sp = base + j;
+                if (sp >= end) break;
+                while (s_rp[t + 1] <= sp) {  // the next tile (empty ones passed over)
+                    flush();
+                    ++t;
+                }
+                bad |= k0[j] < 0 || (k0[j] & 7) || kl[j] < 1 || (int64_t)k0[j] + kl[j] > kv_rows;
+                acc += ((unsigned long long)max(kl[j], 0) + kBN - 1) / kBN;
             }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
-        if (lane == 0) s_n[t] = bad ? -1 : (int32_t)min(n, (int64_t)1 << 24);
+        if (first < end) flush();
     }
+    __syncthreads();
+    for (int t = tid; t < nq; t += kSchedThreads)
+        s_n[t] = !rows_ok || s_f[t] ? -1 : (int32_t)min(s_n64[t], 1ull << 24);
     __syncthreads();
     // W (64-bit: a tile has at most 2^24 steps) and the chunk length
     int64_t mine = 0;
