@@ -87,16 +87,20 @@ def source_sha(path):
 
 
 def traffic_per_launch(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source and on this workload."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256") != source_sha(ATTN_SRC) or t.get("workload", "wan13b_chunk") != workload:
-        return None
-    return t.get("hbm_bytes_per_launch")
+    """HBM bytes per attention launch from a committed rocprofv3 counter summary
+    (profiles/attn_*traffic.json), if one was taken on the current kernel source and on this
+    workload."""
+    import glob
+    sha = source_sha(ATTN_SRC)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "attn_*traffic.json"))):
+        try:
+            with open(path) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if t.get("kernel_source_sha256") == sha and t.get("workload", "wan13b_chunk") == workload:
+            return t.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, inputs, seconds):
