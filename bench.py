@@ -19,8 +19,9 @@ Prints one JSON line.  value = attention FLOP on computed blocks / step time (TF
 step time taken over K steps back to back with HIP events only at the two ends; K more
 steps carry events around each launch, which time the attention kernel alone on its launch
 stream (mean and median, warm caches) and the append (+ plan) launch; --cold-steps more
-steps are each preceded by a 512 MiB scratch write that evicts the MALL and the L2s (cold:
-K/V, Q and plan from HBM).
+steps are each preceded by a read of 512 MiB of scratch that evicts the MALL and the L2s
+(cold: K/V, Q and plan from HBM; --cold-write: a write of the scratch instead, whose dirty
+lines the step then also writes back).
 --library-reference adds the stock library call on the same shapes (torch's SDPA where every
 query sees every cached key; F.linear with --qkv) as context, timed the same way.
 """
@@ -66,7 +67,9 @@ def parse():
     ap.add_argument("--rel-l1", action="store_true",
                     help="time the block-reuse indicator (relative L1 of 30 blocks of 4680 x 1536 bf16 features)")
     ap.add_argument("--cold-steps", type=int, default=5,
-                    help="attention calls timed after a 512 MiB scratch write each (cold MALL and L2); 0: skip")
+                    help="attention calls timed after a 512 MiB scratch sweep each (cold MALL and L2); 0: skip")
+    ap.add_argument("--cold-write", action="store_true",
+                    help="cold steps: the sweep writes the scratch instead of reading it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one device-to-device copy of MIB MiB before timing (HBM counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -448,14 +451,20 @@ def measure(args, name, steps, warmup, cold_steps, tau=None, separate_plan=False
     prep_avg = sum(a.elapsed_time(b) for a, b, _ in events) / steps
     attn_tflops = flop / (attn_avg * 1e-3) / 1e12
 
-    # cold: before each step, a 512 MiB write evicts the 256 MB MALL and the L2s, so the step
-    # reads its K/V, Q and plan from HBM (the scratch write is outside the timed events)
+    # cold: before each step, a sweep over 512 MiB of scratch evicts the 256 MB MALL and the
+    # L2s, so the step reads the cached K/V, Q and the plan from HBM (the sweep is outside the
+    # timed events).  By default the sweep reads (the caches then hold clean lines); with
+    # --cold-write it writes, and the step also pays for writing the scratch's dirty lines back.
     cold = []
     if cold_steps > 0:
-        scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.int32, device="cuda")
+        scratch = torch.ones(512 * 2 ** 20 // 4, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
         cev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(cold_steps)]
         for i in range(cold_steps):
-            scratch.fill_(i)
+            if args.cold_write:
+                scratch.fill_(i)
+            else:
+                scratch.sum(dtype=torch.int64)
             step(cev[i])
         torch.cuda.synchronize()
         cold = [b.elapsed_time(c) for _, b, c in cev]
