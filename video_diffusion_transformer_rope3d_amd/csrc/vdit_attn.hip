@@ -874,6 +874,12 @@ __device__ inline void pipe_load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc
     using P = Pipe<D, NST>;
     constexpr int KRPB = 64 / T::KCH, VRPB = 64 / T::VCH;
     const int last = kend - 1 - k0;
+    // The LDS destinations are recomputed from the stage base at every call (one scalar add
+    // each): seen as loop constants, they are hoisted and kept live through the key loop, one
+    // scalar register per stage and load, which the unit kernel then spills and reloads.
+    int z = 0;
+    asm volatile("" : "+s"(z));
+    smem += z;
     if (kst >= 0) {
         char* kdst = smem + kst * P::K_BYTES;
 #pragma unroll
@@ -1542,8 +1548,9 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
             const int q_start = my_tile >= 0 ? plan_word(qtiles + 2 * my_tile) : 0;
             const int q_len = my_tile >= 0 ? plan_word(qtiles + 2 * my_tile + 1) : 1;
             // uniform per wave: the tile exists and holds some of the wave's 32 rows (a wave past
-            // the end of a short tile keeps its share of the DMA and the barriers, nothing else)
-            const bool active = my_tile >= 0 && uniform(wave % kTileWaves) * 32 < q_len;
+            // the end of a short tile keeps its share of the DMA and the barriers, nothing else);
+            // read as a scalar so that its branches need no saved exec mask
+            const bool active = uniform(my_tile >= 0 && uniform(wave % kTileWaves) * 32 < q_len ? 1 : 0) != 0;
             const int r_in = (wave % kTileWaves) * 32 + qi;
             const bool row_valid = active && r_in < q_len;
             const int row = q_start + (r_in < q_len ? r_in : q_len - 1);
