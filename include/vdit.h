@@ -268,7 +268,13 @@ int vdit_plan_dynamic(const vdit_mask_cfg* base, const vdit_dynamic_cfg* dyn, vd
  *   rounding to bf16); with rope == NULL they are used as given (rounded to bf16).
  * plan_dev: device plan built for this rule, grid, q_t0 and the cache's current slots
  *   (by vdit_plan_mask, or by vdit_plan_dynamic with base = this rule, in which case
- *   mask->kind carries VDIT_MASK_FLAG_DYNAMIC).
+ *   mask->kind carries VDIT_MASK_FLAG_DYNAMIC).  The plan is read on the device only: the
+ *   kernels check its magic, its kind (flag included) and tile against this call's rule, its
+ *   tile count against this grid, and every span against the cache (inside it, 8-aligned,
+ *   non-empty).  What fails is not computed: the outputs it would have written are NaN
+ *   (all of them for a bad header; the query tile's rows for a bad span under the
+ *   log-radial and dynamic rules) and the call still returns VDIT_OK.  A plan of the same
+ *   rule and tile count built for another q_t0 or slot table is not detected.
  * softmax_scale <= 0 selects 1/sqrt(head_dim).
  * o: same shape as q, bf16 or fp32 (device).  lse: NULL or device fp32 [heads][tokens],
  *   natural-log log-sum-exp of each row's scaled logits (-inf for a row with no visible

@@ -413,12 +413,13 @@ def test_split_stream_path_is_taken():
 
 
 @pytest.mark.parametrize("name,corrupt,dyn", [("small_chunk_pad", "magic", False), ("small_chunk_pad", "tiles", False),
-                                              ("small_chunk_pad", "span", False), ("small_radial", "magic", False),
-                                              ("small_radial", "span", False), ("small_chunk_pad", "magic", True),
-                                              ("small_chunk_pad", "span", True)])
+                                              ("small_chunk_pad", "span", False), ("small_chunk_pad", "kind", False),
+                                              ("small_radial", "magic", False), ("small_radial", "span", False),
+                                              ("small_radial", "tile", False), ("small_chunk_pad", "magic", True),
+                                              ("small_chunk_pad", "span", True), ("small_chunk_pad", "kind", True)])
 def test_rejected_plan_gives_nan_outputs(name, corrupt, dyn):
-    """A plan that does not belong to the call (wrong magic, another tile count, a span past the
-    cache) is not computed.  The check is in the kernel, which exits normally, so the call returns
+    """A plan that does not belong to the call (wrong magic, another rule or tile size, another tile
+    count, a span past the cache) is not computed.  The check is in the kernel, which exits normally, so the call returns
     OK; the outputs it did not compute are NaN.  A bad header, or a bad span under the unit
     kernel (every workgroup validates the whole plan), poisons every output; under the tile
     kernel a bad span poisons its own query tile, here tile 0 of every head.  With the dynamic
@@ -429,11 +430,17 @@ def test_rejected_plan_gives_nan_outputs(name, corrupt, dyn):
     r = run_workload(w, inp)
     s = r["session"]
     bad = r["plan"].clone()
+    if dyn:  # the static plan's words as a dynamic plan of the same rule would carry them
+        bad[2] |= B.VDIT_MASK_FLAG_DYNAMIC
     nq = int(bad[4].item())
     if corrupt == "magic":
         bad[0] = 0
     elif corrupt == "tiles":
         bad[4] = nq + 1
+    elif corrupt == "kind":  # a plan of another rule: the static plan under the dynamic mask, else another rule
+        bad[2] = int(r["plan"][2].item()) if dyn else int(r["plan"][2].item()) ^ 1
+    elif corrupt == "tile":
+        bad[3] = int(bad[3].item()) // 2
     else:  # the first span of tile 0 starts at the end of the cache (8-aligned, outside it)
         bad[8 + 3 * nq + 1] = s.cache.kv_rows
     lse = torch.zeros((w.heads, w.n_q), dtype=torch.float32, device="cuda")
@@ -468,14 +475,18 @@ def test_query_tile_without_keys(dyn):
     rp2[drop + 1:] -= rp[drop + 1] - rp[drop]
     hdr = p[:8].copy()
     hdr[5] = len(keep)
+    if dyn:  # the words a dynamic plan of the same rule would carry
+        hdr[2] |= B.VDIT_MASK_FLAG_DYNAMIC
     words = np.concatenate([hdr, qt.ravel(), rp2, sp[keep].ravel()]).astype(np.int32)
     plan2 = torch.from_numpy(words).to("cuda")
     mask = B.dynamic_mask(r["session"].mask) if dyn else None
     lse = torch.empty((w.heads, w.n_q), dtype=torch.float32, device="cuda")
     o = r["session"].attend(r["q"], w.q_frames, w.q_t0, plan2, lse=lse, mask=mask)
     if dyn:
+        ref_plan = r["plan"].clone()
+        ref_plan[2] |= B.VDIT_MASK_FLAG_DYNAMIC
         ref_lse = torch.empty_like(lse)
-        ref_o = r["session"].attend(r["q"], w.q_frames, w.q_t0, r["plan"], lse=ref_lse, mask=mask)
+        ref_o = r["session"].attend(r["q"], w.q_frames, w.q_t0, ref_plan, lse=ref_lse, mask=mask)
     else:
         ref_o, ref_lse = r["o"], r["lse"]
     torch.cuda.synchronize()

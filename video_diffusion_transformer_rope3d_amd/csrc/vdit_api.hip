@@ -568,6 +568,8 @@ int attn_fwd_impl(vdit_tensor q, const vdit_rope_cfg* rope, vdit_grid q_grid, in
     a.head_dim = cache->head_dim;
     a.n_qtiles = plan_qtile_count(g);
     a.mask_kind = mask->kind;
+    a.plan_kind = mask_in->kind;  // the dynamic flag included
+    a.plan_tile = g.tile;
     a.unpaired = unpaired;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     if (n == 0 || a.n_qtiles == 0) return ok();

@@ -76,6 +76,7 @@ struct AttnArgs {
     RopeDev rope;
     int32_t has_rope;
     int32_t hw, wf, t0, n_tokens, heads, n_qtiles;
+    int32_t plan_kind, plan_tile;  // header words 2 and 3 of the call's plan
     float scale_log2;
     int32_t* cnt;  // per-tile arrival counters, zero between calls
     float* part;   // partial results, two slots per workgroup
@@ -1090,8 +1091,9 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
 
     const int32_t* plan = a.plan;
     const int nq = plan[4];
-    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || nq != a.n_qtiles) {
+    // a plan that does not belong to this call (another magic, rule, tile size or tile count) is
+    // not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[2] != a.plan_kind || plan[3] != a.plan_tile || nq != a.n_qtiles) {
         poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
         return;
     }
@@ -1297,8 +1299,10 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
 
     const int32_t* plan = a.plan;
     const int nq = a.n_qtiles;
-    // a plan that does not belong to this call is not read out of bounds: NaN outputs instead
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[4] != nq || nq > kMaxTiles) {
+    // a plan that does not belong to this call (another magic, rule, tile size or tile count) is
+    // not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[2] != a.plan_kind || plan[3] != a.plan_tile || plan[4] != nq ||
+        nq > kMaxTiles) {
         poison_share<D, OF32>(a, blockIdx.x, G);
         return;
     }
@@ -1853,6 +1857,8 @@ hipError_t launch_attn_fwd(const AttnLaunch& L, hipStream_t s) {
     a.n_tokens = L.n_tokens;
     a.heads = L.heads;
     a.n_qtiles = L.n_qtiles;
+    a.plan_kind = L.plan_kind;
+    a.plan_tile = L.plan_tile;
     a.scale_log2 = L.scale_log2;
     if (L.head_dim == 128) return launch_d<128>(L, a, s);
     return launch_d<64>(L, a, s);

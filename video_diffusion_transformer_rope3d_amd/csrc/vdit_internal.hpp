@@ -223,6 +223,7 @@ struct AttnLaunch {
     bool has_rope;
     int32_t hw, wf, t0, n_tokens, heads, head_dim, n_qtiles;
     int32_t mask_kind;
+    int32_t plan_kind, plan_tile;  // header words 2 and 3 the call's plan must carry
     bool unpaired;  // plan from vdit_plan_dynamic: neighbouring tiles do not share span lists
     float scale_log2;
     void* workspace;  // caller-owned, attn_workspace_bytes
