@@ -272,6 +272,22 @@ def test_attention_parity_sampled(name):
         np.testing.assert_allclose(lse[h, rows], ref[h][1], atol=1e-2, rtol=0)
 
 
+def test_attention_parity_headline_every_row():
+    """The benchmark's workload (Wan-1.3B chunk: 12 heads, 4680 queries, 14040 cached keys), in the
+    benchmark's launch configuration: every output element and every LSE against the oracle, not
+    a sample (the oracle takes about a second per head)."""
+    _print("attention every row", "wan13b_chunk")
+    w = get_workload("wan13b_chunk")
+    inp = make_inputs(w)
+    r = run_workload(w, inp)
+    o = r["o"].float().cpu().numpy()
+    lse = r["lse"].cpu().numpy()
+    ref = _oracle_rows(w, inp, range(w.heads), np.arange(w.n_q))
+    for h in range(w.heads):
+        compare(o[:, h], ref[h][0], what=f"wan13b_chunk every row, head {h}")
+        np.testing.assert_allclose(lse[h], ref[h][1], atol=1e-2, rtol=0)
+
+
 @pytest.mark.parametrize("name", ["small_radial", "small_chunk_pad", "stream_wrap_straddle", "small_stream_radial"])
 def test_zero_queries_average_visible_values(name):
     """Q = 0: every visible key gets the same weight, so O = mean of the visible V rows."""
