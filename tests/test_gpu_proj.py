@@ -51,10 +51,41 @@ def _tol(x, w, b, ref, c, rotated):
 @pytest.mark.parametrize("name", list(CASES))
 def test_qkv_rope_append_matches_oracle(name):
     print("qkv", name, flush=True)
-    h, d, c, fh, fw, frames, t0, cap, hist, bias, dims = CASES[name]
+    _check_case(CASES[name], seed=len(name))
+
+
+def _random_case(i):
+    """Seeded random geometry: heads x head_dim a multiple of 128 (the entry point's rule), hidden a
+    multiple of 64, ragged token tiles, earlier appends that may wrap the ring, bias and RoPE on or off."""
+    rng = np.random.default_rng(5000 + i)
+    d = int(rng.choice([64, 128]))
+    h = int(rng.choice([2, 4])) if d == 64 else int(rng.choice([1, 2, 3]))
+    c = 64 * int(rng.integers(1, 9))
+    fh, fw = int(rng.integers(2, 13)), int(rng.integers(2, 15))
+    frames = int(rng.integers(1, 5))
+    cap = frames + int(rng.integers(0, 5))
+    start, n_hist = int(rng.integers(0, 25)), int(rng.integers(0, cap + 3))
+    hist, t = [], start
+    while t < start + n_hist:
+        f = min(int(rng.integers(1, 4)), start + n_hist - t, cap)
+        hist.append((t, f))
+        t += f
+    dims = None if rng.random() < 0.2 else ((24, 20, 20) if d == 64 else (44, 42, 42))
+    return (h, d, c, fh, fw, frames, start + n_hist, cap, hist, bool(rng.random() < 0.5), dims)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_qkv_rope_append_random_geometry(case):
+    geom = _random_case(case)
+    print("qkv random", case, geom, flush=True)
+    _check_case(geom, seed=300 + case)
+
+
+def _check_case(geom, seed):
+    h, d, c, fh, fw, frames, t0, cap, hist, bias, dims = geom
     hw = fh * fw
     n = frames * hw
-    x, w, b = _inputs(h, d, c, n, bias, seed=len(name))
+    x, w, b = _inputs(h, d, c, n, bias, seed=seed)
     theta = 1e4
     rope = B.Rope(d, dims, theta, t0 + frames + 4, fh, fw) if dims else None
     cache = B.KVCache(cap, hw, h, d)

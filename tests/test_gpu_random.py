@@ -44,7 +44,7 @@ def random_workload(i: int) -> Workload:
     start = int(rng.integers(0, 30))
     history, t = [], start
     while t < start + n_hist:
-        f = min(int(rng.integers(1, 4)), start + n_hist - t)
+        f = min(int(rng.integers(1, 4)), start + n_hist - t, capacity)
         history.append((t, f))
         t += f
     mask = MaskSpec(kind, chunk_frames=cf, tile=128, radial_w0=int(rng.integers(1, 6)), radial_decay_log2=1,
