@@ -7,6 +7,7 @@ import numpy as np
 import torch
 
 import oracle
+from workloads.configs import MaskSpec, Workload
 from video_diffusion_transformer_rope3d_amd import AttentionSession
 from video_diffusion_transformer_rope3d_amd import binding as B
 
@@ -83,3 +84,30 @@ def compare(o_gpu, o_ref, max_abs=MAX_ABS, rel_l2=REL_L2, what=""):
     MARGINS.append((test, what, err, rel, max_abs, rel_l2))
     assert err <= max_abs and rel <= rel_l2, f"{what}: max-abs {err:.3e} (<= {max_abs}), rel-L2 {rel:.3e} (<= {rel_l2})"
     return err, rel
+
+
+def random_workload(i: int) -> Workload:
+    """Seeded random geometry for the parity tests: heads, head_dim, frame shape (ragged tiles), mask
+    rule, chunk length, ring capacity, history (wrapping the ring or not), dtype and data scale."""
+    rng = np.random.default_rng(7000 + i)
+    d = int(rng.choice([64, 128]))
+    dims = (24, 20, 20) if d == 64 else (44, 42, 42)
+    kind = str(rng.choice(["dense", "chunk_causal", "log_radial", "log_radial_causal"]))
+    cf = int(rng.integers(1, 4))
+    causal = kind in ("chunk_causal", "log_radial_causal")
+    q_frames = cf * int(rng.integers(1, 3)) if causal else int(rng.integers(1, 5))
+    capacity = q_frames + int(rng.integers(0, 7))
+    n_hist = int(rng.integers(0, capacity - q_frames + 5))  # past capacity - q_frames: the ring wraps
+    start = int(rng.integers(0, 30))
+    history, t = [], start
+    while t < start + n_hist:
+        f = min(int(rng.integers(1, 4)), start + n_hist - t, capacity)
+        history.append((t, f))
+        t += f
+    mask = MaskSpec(kind, chunk_frames=cf, tile=128, radial_w0=int(rng.integers(1, 6)), radial_decay_log2=1,
+                    long_range_period=int(rng.choice([0, 2, 4])))
+    return Workload(
+        name=f"random_{i}", description="seeded random geometry", heads=int(rng.choice([1, 2, 3, 5])), head_dim=d,
+        frame_h=int(rng.integers(2, 25)), frame_w=int(rng.integers(2, 33)), q_frames=q_frames, q_t0=start + n_hist,
+        rope_dims=dims, theta=1e4, mask=mask, capacity=capacity, history=tuple(history),
+        dtype="fp32" if rng.random() < 0.2 else "bf16", data_scale=float(rng.choice([1.0, 0.3])), seed=9000 + i)

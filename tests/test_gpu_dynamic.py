@@ -25,7 +25,7 @@ from workloads import get_workload, make_inputs
 from workloads.synth import bf16_round
 from video_diffusion_transformer_rope3d_amd import binding as B
 
-from harness import compare, device_plan_words, run_workload
+from harness import compare, device_plan_words, random_workload, run_workload
 from schedule_model import item_start, tile_steps_from_plan, tile_work_list
 
 pytestmark = pytest.mark.gpu
@@ -70,10 +70,24 @@ def _kept_f32(p, cand, tau):
         return cand & ((p - small[:, None]) >= cut[:, None])
 
 
+# seeded random geometries (every rule, ragged tiles, ring wrap) with seeded thresholds
+RANDOM = [(i, float(np.random.default_rng(40 + i).uniform(0.0, 1.0))) for i in range(100, 108)]
+
+
 @pytest.mark.parametrize("name,tau", CASES)
 def test_dynamic_plan_matches_oracle(name, tau):
     print("dynamic plan", name, tau, flush=True)
-    w = get_workload(name)
+    _check_dynamic_plan(get_workload(name), tau)
+
+
+@pytest.mark.parametrize("case,tau", RANDOM)
+def test_dynamic_plan_random_geometry(case, tau):
+    w = random_workload(case)
+    print("dynamic plan random", case, tau, w, flush=True)
+    _check_dynamic_plan(w, tau)
+
+
+def _check_dynamic_plan(w, tau):
     inp = make_inputs(w)
     r, plan, prox, tpf = _device_dynamic(w, inp, tau)
     st = oracle.build_state(w, inp)
@@ -138,6 +152,17 @@ def test_attention_on_a_dynamic_plan(name, tau):
     attention over exactly the keys the plan keeps."""
     print("attention on dynamic plan", name, tau, flush=True)
     w = get_workload(name)
+    _check_attention_on_dynamic(w, tau, split_expected=name == "wan13b_chunk_h2")
+
+
+@pytest.mark.parametrize("case,tau", RANDOM)
+def test_attention_on_a_dynamic_plan_random_geometry(case, tau):
+    w = random_workload(case)
+    print("attention on dynamic plan random", case, tau, w, flush=True)
+    _check_attention_on_dynamic(w, tau, split_expected=False)
+
+
+def _check_attention_on_dynamic(w, tau, split_expected):
     inp = make_inputs(w)
     r, plan, _, _ = _device_dynamic(w, inp, tau)
     s = r["session"]
@@ -156,7 +181,7 @@ def test_attention_on_a_dynamic_plan(name, tau):
     o_gpu = o.float().cpu().numpy()
     for h in range(w.heads):
         ref, ref_lse = oracle.masked_attention(q_rot[:, h], st.k[:, h], st.v[:, h], allowed, w.head_dim ** -0.5)
-        compare(o_gpu[:, h], ref, what=f"{name} tau {tau} head {h}")
+        compare(o_gpu[:, h], ref, what=f"{w.name} tau {tau} head {h}")
         np.testing.assert_allclose(lse.cpu().numpy()[h], ref_lse, atol=1e-2, rtol=0)
     # the work list the call ran: the host model's, up to the order of equal lengths
     want, _ = tile_work_list(tile_steps_from_plan(qt.tolist(), rp.tolist(), sp.tolist()), w.heads)
@@ -169,5 +194,5 @@ def test_attention_on_a_dynamic_plan(name, tau):
     for it in raw.tolist():  # each item's first key step located in the plan's spans
         assert tuple(it[6:]) == item_start(rpl, spl, it[0], it[1])
     assert [min(it[2] - it[1], 1023) for it in got] == [min(it[2] - it[1], 1023) for it in want]
-    if name == "wan13b_chunk_h2":  # long tiles: chunks and their merge are exercised
+    if split_expected:  # long tiles: chunks and their merge are exercised
         assert any(it[5] > 1 for it in got)
