@@ -7,11 +7,13 @@
 // v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  With W as the A operand every lane owns
 // one token and holds the channels (r % 4) + 8 (r / 4) + 4 (lane / 32) of a 32-channel
 // block in its 16 accumulators, so the pairs (2i, 2i + 1) that RoPE rotates are in the same
-// lane.  A workgroup computes 128 features x 128 tokens (4 waves of 64 x 64); with
+// lane.  A workgroup computes 128 features x 192 tokens (4 waves of 64 x 96); with
 // head_dim 128 the features are one head of Q, K or V.  W and x tiles of 64 channels go from
 // global memory straight to LDS (buffer loads into LDS, XOR-swizzled rows) in two stages, so
-// the loads of the next k-step are in flight while one is computed.  Two workgroups share a
-// CU (64 KB of LDS each), so one's epilogue and barrier waits overlap the other's MFMAs.
+// the loads of the next k-step are in flight while one is computed.  The bytes a k-step moves
+// into LDS are what bounds the loop, so the token tile is as long as two 40 KB stages allow at
+// two workgroups per CU (80 KB of LDS each); one's epilogue and barrier waits overlap the
+// other's MFMAs.
 // Epilogue: + bias, rotation of Q and K at (t0 + f, h, w) in fp32, one rounding to bf16;
 // Q to its output, K to the ring's K rows, V to the ring's transposed V rows.
 #include "vdit_bf16.hpp"
@@ -25,13 +27,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kPN = 128;                 // features per tile
-constexpr int kPM = 128;                 // tokens per tile
+constexpr int kPM = 192;                 // tokens per tile
 constexpr int kPK = 64;                  // hidden channels per k-step
 constexpr int kPWaves = 4;
 constexpr int kPThreads = kPWaves * 64;
 constexpr int kRowBytes = kPK * 2;       // 128 bytes per tile row
 constexpr int kWBytes = kPN * kRowBytes;  // 16 KB
-constexpr int kXBytes = kPM * kRowBytes;  // 16 KB
+constexpr int kXBytes = kPM * kRowBytes;  // 24 KB
+constexpr int kTBW = kPM / 64;           // 32-token blocks per wave (two waves per token half)
 constexpr int kStage = kWBytes + kXBytes;
 constexpr int kNStage = 2;               // the next k-step is in flight
 constexpr int kWLoads = kWBytes / 1024 / kPWaves, kXLoads = kXBytes / 1024 / kPWaves;  // per thread
@@ -131,26 +134,25 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
     // fragments: row r of a tile, chunk c (8 channels) at r * 128 + ((c ^ swz(r)) * 16)
     const int sw = (li >> 1) & 7;
     const int wf_row = 64 * (wave & 1) + li;   // W rows of this wave (+ 32 fb)
-    const int xt_row = 64 * (wave >> 1) + li;  // x rows of this wave (+ 32 tb); wave >> 1 in 0..1
-    f32x16 acc[2][2];
+    const int xt_row = (kPM / 2) * (wave >> 1) + li;  // x rows of this wave (+ 32 tb); wave >> 1 in 0..1
+    f32x16 acc[2][kTBW];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < kTBW; ++j) acc[i][j] = f32x16{};
 
-    // Epilogue inputs, loaded now so the k-loop hides their latency: the tile's bias and, for Q
-    // and K, the (cos, sin) of every channel pair this lane will rotate.
+    // The wave's place in the tile and in the Q, K, V layout, and the epilogue's bias.
     const int hd = a.heads * a.head_dim;
     const int part = n0 / hd;  // 0: Q, 1: K, 2: V (a tile never straddles two)
     const int fcol0 = 64 * (wave & 1);        // the wave's first feature inside the tile
-    const int mrow0 = m0 + 64 * (wave >> 1);  // the wave's first token
+    const int mrow0 = m0 + (kPM / 2) * (wave >> 1);  // the wave's first token
     const int c_w = n0 + fcol0 - part * hd;   // first channel of the wave inside its part
     const int h = c_w / a.head_dim, d_w = c_w - h * a.head_dim;
     const bool rot = part < 2 && a.has_rope;
     float bias_r[2][4][4];  // [channel block][group of 4][channel]: the lane's 32 channels
-    float2 cs[2][2][4][2];  // [token block][channel block][group of 4][pair]
-    // Issued in the first k-step before its DMA: vmcnt counts loads in order, so loads issued
-    // before the stage loads would be waited for at the first stage wait.
+    // Loaded at the start of the last k-step, which issues no DMA: the registers are free
+    // through the loop and the loads land during that k-step's MFMAs.  The (cos, sin) tables
+    // are read per token block in the epilogue.
     auto load_epilogue_inputs = [&]() {
 #pragma unroll
         for (int f = 0; f < 2; ++f)
@@ -159,22 +161,6 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     bias_r[f][q4][e] = a.bias ? a.bias[n0 + fcol0 + 32 * f + 8 * q4 + 4 * g + e] : 0.f;
-        if (rot) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int m = min(mrow0 + 32 * t + li, a.n_tokens - 1);
-                const int fr = m / a.hw, sp = m - fr * a.hw;
-                const int tg = a.t0 + fr, ph = sp / a.wf, pw = sp - ph * a.wf;
-#pragma unroll
-                for (int f = 0; f < 2; ++f)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            cs[t][f][q4][e] =
-                                rope_cs(a.rope, (d_w + 32 * f + 8 * q4 + 4 * g + 2 * e) >> 1, tg, ph, pw);
-            }
-        }
     };
 
     const int nk = a.hidden / kPK;
@@ -184,18 +170,19 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
     int st = 0;
     for (int kk = 0; kk < nk; ++kk) {
         char* cur = smem + st * kStage;
-        if (kk == 0) load_epilogue_inputs();
+        if (kk == nk - 1) load_epilogue_inputs();
         // the other stage was consumed before the last barrier
         if (kk + 1 < nk) load_stage(kk + 1, smem + (st ^ 1) * kStage);
         // fragments of 16-channel step j + 1 are read while the MFMAs of step j run
-        bf16x8 af[2][2], bf[2][2];
+        bf16x8 af[2][2], bf[2][kTBW];
         auto read_frags = [&](int j, int b) {
             const int coff = (((2 * j + g) ^ sw) * 16);
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
+            for (int f = 0; f < 2; ++f)
                 af[b][f] = *reinterpret_cast<const bf16x8*>(cur + (wf_row + 32 * f) * kRowBytes + coff);
-                bf[b][f] = *reinterpret_cast<const bf16x8*>(cur + kWBytes + (xt_row + 32 * f) * kRowBytes + coff);
-            }
+#pragma unroll
+            for (int tb = 0; tb < kTBW; ++tb)
+                bf[b][tb] = *reinterpret_cast<const bf16x8*>(cur + kWBytes + (xt_row + 32 * tb) * kRowBytes + coff);
         };
         read_frags(0, 0);
 #pragma unroll
@@ -204,14 +191,15 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) acc[f][t] = mfma32(af[j & 1][f], bf[j & 1][t], acc[f][t]);
-            // issue order: one fragment read of step j + 1, one MFMA of step j, four times
+                for (int t = 0; t < kTBW; ++t) acc[f][t] = mfma32(af[j & 1][f], bf[j & 1][t], acc[f][t]);
+            // issue order: one fragment read of step j + 1, one MFMA of step j, then the last MFMA
             if (j + 1 < kPK / 16) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 2 + kTBW; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * kTBW - 2 - kTBW, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -224,13 +212,29 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
     }
 
     // ---- epilogue.  The stages are free (the loop ended on a barrier).  Each wave turns its
-    // 64 x 64 block into bf16 (+ bias, RoPE) in an LDS region of its own, token rows for Q and
-    // K, channel rows for V, then writes whole 128-byte rows to global memory.
-    constexpr int kPitch = 136;  // bytes per LDS row: 64 bf16 and 8 bytes of padding
-    char* region = smem + wave * 64 * kPitch;
+    // 64 x 96 block into bf16 (+ bias, RoPE) in an LDS region of its own, token rows for Q and
+    // K, channel rows for V, then writes whole rows to global memory (128 bytes per token for Q
+    // and K, 16 bytes per 8 tokens of a V^T row).
+    constexpr int kPitch = 136;                   // Q, K: token rows of 64 bf16 and 8 bytes of padding
+    constexpr int kVPitch = (kPM / 2) * 2 + 8;    // V: channel rows of the wave's tokens and 8 bytes of padding
+    constexpr int kRegion = (kPM / 2) * kPitch > 64 * kVPitch ? (kPM / 2) * kPitch : 64 * kVPitch;
+    char* region = smem + wave * kRegion;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTBW; ++t) {
         const int ml = 32 * t + li;
+        float2 cs[2][4][2];  // this token block's (cos, sin): [channel block][group of 4][pair]
+        if (rot) {
+            const int m = min(mrow0 + ml, a.n_tokens - 1);
+            const int fr = m / a.hw, sp = m - fr * a.hw;
+            const int tg = a.t0 + fr, ph = sp / a.wf, pw = sp - ph * a.wf;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        cs[f][q4][e] = rope_cs(a.rope, (d_w + 32 * f + 8 * q4 + 4 * g + 2 * e) >> 1, tg, ph, pw);
+        }
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
 #pragma unroll
@@ -241,12 +245,12 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
                 for (int e = 0; e < 4; ++e) y[e] = acc[f][t][4 * q4 + e] + bias_r[f][q4][e];
                 if (rot) {
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) rope_apply(cs[t][f][q4][e], y[2 * e], y[2 * e + 1]);
+                    for (int e = 0; e < 2; ++e) rope_apply(cs[f][q4][e], y[2 * e], y[2 * e + 1]);
                 }
                 if (part == 2) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        *reinterpret_cast<uint16_t*>(region + (cl + e) * kPitch + ml * 2) =
+                        *reinterpret_cast<uint16_t*>(region + (cl + e) * kVPitch + ml * 2) =
                             (uint16_t)(pack_bf16x2(y[e], 0.f) & 0xffffu);
                 } else {
                     *reinterpret_cast<uint2*>(region + ml * kPitch + cl * 2) =
@@ -256,14 +260,14 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
         }
     }
     __syncthreads();
-    // read back 16 bytes (8 elements of a row) per lane, 8 rows of 128 bytes per pass
+    if (part < 2) {
+        // token rows: 8 lanes write one token's 64 channels (128 bytes)
 #pragma unroll
-    for (int pass = 0; pass < 8; ++pass) {
-        const int row = pass * 8 + (lane >> 3), ch = (lane & 7) * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(region + row * kPitch + ch * 2);
-        if (part < 2) {  // row = token, ch = channel
+        for (int pass = 0; pass < kPM / 16; ++pass) {
+            const int row = pass * 8 + (lane >> 3), ch = (lane & 7) * 8;
             const int m = mrow0 + row;
             if (m >= a.n_tokens) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(region + row * kPitch + ch * 2);
             uint16_t* dst;
             if (part == 0) {
                 dst = a.q + (int64_t)m * a.q_st + (int64_t)h * a.q_sh + d_w + ch;
@@ -273,8 +277,17 @@ __global__ __launch_bounds__(kPThreads, 2) void qkv_rope_append_kernel(ProjArgs 
                 dst = a.kc + ((int64_t)h * a.kv_rows + phys) * a.head_dim + d_w + ch;
             }
             *reinterpret_cast<uint4*>(dst) = v;
-        } else {  // row = channel, ch = first of 8 tokens
+        }
+    } else {
+        // channel rows: each 16 bytes hold 8 consecutive tokens of one channel
+        constexpr int kChunks = kPM / 16;  // 16-byte chunks per channel row
+#pragma unroll
+        for (int pass = 0; pass < kChunks; ++pass) {
+            const int c = pass * 64 + lane;
+            const int row = c / kChunks, ch = (c % kChunks) * 8;
             const int m = mrow0 + ch;
+            if (m >= a.n_tokens) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(region + row * kVPitch + ch * 2);
             const int fr = m / a.hw, sp = m - fr * a.hw;
             uint16_t* dst = a.vt + ((int64_t)h * a.head_dim + d_w + row) * a.kv_rows;
             const int64_t phys = (int64_t)((a.t0 + fr) % a.capacity) * a.frame_stride + sp;
