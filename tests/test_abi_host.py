@@ -257,6 +257,28 @@ def test_attention_errors(L):
                                  None, None, 0, None) == B.VDIT_ERR_INVALID_ARG
 
 
+def test_attention_query_tile_limit(L):
+    """One attention call holds at most 4096 query tiles (the unit kernel's table lives in LDS):
+    a call one frame past it is refused as unsupported before any launch, and a call of exactly
+    4096 tiles passes that check (it then stops at the device query without a GPU, or at the
+    missing workspace with one)."""
+    fake = 0x10000  # never dereferenced: both calls fail validation
+    m = B.mask_cfg("chunk_causal", 1)
+    t = B.VditTensor(fake, B.VDIT_DTYPE_BF16, 0, 128, 64)
+    slots = np.array([0, 1, 2, 3, 4], np.int32)
+    # 256 x 512 tokens per frame = 1024 tiles of 128 rows per frame
+    desc = B.VditKVCache(fake, fake, fake, slots.ctypes.data, 5, 256 * 512, 2, 64)
+    n = ctypes.c_int32(0)
+    assert L.vdit_plan_qtiles(ctypes.byref(m), B.grid(4, 256, 512), 0, ctypes.byref(n)) == 0 and n.value == 4096
+    over = L.vdit_block_attn_fwd(t, None, B.grid(5, 256, 512), 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
+                                 None, None, 0, None)
+    assert over == B.VDIT_ERR_UNSUPPORTED
+    assert b"5120 query tiles" in L.vdit_last_error()
+    at = L.vdit_block_attn_fwd(t, None, B.grid(4, 256, 512), 0, ctypes.byref(desc), ctypes.byref(m), fake, 0.0, t,
+                               None, None, 0, None)
+    assert at in (B.VDIT_ERR_DEVICE, B.VDIT_ERR_BUFFER_TOO_SMALL)
+
+
 def test_workspace_size_queries_and_short_workspaces(L):
     """The calls that need scratch memory take it from the caller: their size queries are host
     arithmetic (the attention call's unit-kernel plans also ask the device's CU count, which a
