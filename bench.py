@@ -64,6 +64,8 @@ def parse():
                     help="target CPU time of the oracle sample (whole heads are added until reached)")
     ap.add_argument("--qkv", action="store_true",
                     help="time the fused QKV projection + RoPE + K/V append of the Wan-1.3B chunk")
+    ap.add_argument("--rope", action="store_true",
+                    help="time the standalone RoPE3D rotation of the Wan-1.3B chunk's Q and K (in place)")
     ap.add_argument("--rel-l1", action="store_true",
                     help="time the block-reuse indicator (relative L1 of 30 blocks of 4680 x 1536 bf16 features)")
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -284,6 +286,58 @@ def bench_rel_l1(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(gbs / 8000.0, 4), "traffic": None},
         "mean_rel_l1": float(out[-1].item()),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_rope(args):
+    """The standalone RoPE3D rotation (vdit_rope3d_qk) of one Wan-1.3B-shaped chunk: Q and K
+    [4680 x 12 x 128] bf16 rotated in place at global positions (6 + f, h, w), split 44/42/42.
+    HBM-bound: each element read and written once.  On the hot path the same rotation is fused
+    into the attention's Q load and the K/V append; this times it on its own."""
+    import torch
+
+    from video_diffusion_transformer_rope3d_amd import binding as B
+
+    heads, d, fh, fw, frames, t0 = 12, 128, 30, 52, 3, 6
+    n = frames * fh * fw
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn((n, heads, d), device="cuda", generator=gen).to(torch.bfloat16)
+    k = torch.randn((n, heads, d), device="cuda", generator=gen).to(torch.bfloat16)
+    rope = B.Rope(d, (44, 42, 42), 1e4, t0 + frames + 4, fh, fw)
+    grid = B.grid(frames, fh, fw)
+    stream = torch.cuda.current_stream()
+    call = lambda: B.vdit_rope3d_qk(rope, grid, t0, heads, q=q, k=k)  # noqa: E731 (repeated rotations: timing only)
+    clock_ramp(call)
+    for _ in range(args.warmup):
+        call()
+    ms = time_back_to_back(call, args.steps, stream)
+    nbytes = 2 * 2 * n * heads * d * 2  # Q and K, read and written
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        rows = 520  # a bounded sample: the first third of a frame
+        xs = q[:rows].float().cpu().numpy().astype(np.float64)
+        pos = oracle.token_positions(frames, fh, fw, t0)[:rows]
+        t_start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t_start < min(args.cpu_seconds, 10.0):
+            oracle.rope3d(xs, pos, (44, 42, 42), 1e4)
+            reps += 1
+        sec = (time.perf_counter() - t_start) / reps
+        cpu = {"value": round(rows * heads * d * 2 * 2 / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{rows} tokens of Q (bf16 values in fp64, read and written), {reps} passes"}
+    result = {
+        "metric": "standalone RoPE3D rotation: bytes read and written per second", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_ramp_ms": RAMP_SECONDS * 1e3, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan13b_chunk_rope", "tokens": n, "heads": heads, "head_dim": d, "t0": t0},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -527,6 +581,12 @@ def main():
             print("bench.py measures one GPU only", file=sys.stderr)
             sys.exit(2)
         bench_qkv(args)
+        return
+    if args.rope:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_rope(args)
         return
     if args.rel_l1:
         if args.gpus != 1:

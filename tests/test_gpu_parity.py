@@ -207,6 +207,34 @@ def test_rope_inplace_vs_oracle(dtype):
         compare(got, ref, what="rope bf16")
 
 
+@pytest.mark.parametrize("qdt,kdt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                     (torch.float32, torch.bfloat16)])
+def test_rope_q_and_k_in_one_call(qdt, kdt):
+    """Q and K rotated by one call: one launch when their dtypes match (K's rows in the grid's
+    second row), two otherwise.  K is a strided view (every other token row of a wider buffer,
+    heads 3 apart), Q a plain tensor; each must equal the oracle at its own layout."""
+    rng = np.random.default_rng(11)
+    fr, hgt, wid, t0, heads = 2, 7, 9, 13, 3  # 126 tokens: ragged against the 256-thread blocks
+    n = fr * hgt * wid
+    q = to_dev(rng.standard_normal((n, heads, 64)).astype(np.float32), qdt)
+    wide = to_dev(rng.standard_normal((n, 2 * heads, 64)).astype(np.float32), kdt)
+    k = wide[:, :heads]  # token stride 2 * heads * 64, head stride 64
+    q0 = q.float().cpu().numpy().astype(np.float64)
+    k0 = k.float().cpu().numpy().astype(np.float64)
+    rest0 = wide[:, heads:].float().cpu().numpy()
+    rope = B.Rope(64, (24, 20, 20), 1e4, 20, hgt, wid)
+    B.vdit_rope3d_qk(rope, B.grid(fr, hgt, wid), t0, heads, q=q, k=k)
+    pos = oracle.token_positions(fr, hgt, wid, t0)
+    for got, start, dt in ((q, q0, qdt), (k, k0, kdt)):
+        ref = oracle.rope3d(start, pos, (24, 20, 20), 1e4)
+        g = got.float().cpu().numpy()
+        if dt == torch.float32:
+            assert np.abs(g - ref).max() < 2e-5
+        else:
+            assert (np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
+    assert np.array_equal(wide[:, heads:].float().cpu().numpy(), rest0)  # the other heads untouched
+
+
 @pytest.mark.parametrize("name", ["tiny", "small_chunk_pad"])
 def test_kv_append_cache_contents(name):
     w = get_workload(name)

@@ -268,11 +268,15 @@ int vdit_rope3d_qk(const vdit_rope_cfg* cfg, vdit_grid grid, int32_t t0, int32_t
     if (n == 0) return ok();
     RopeDev r = rope_dev(cfg);
     hipStream_t s = (hipStream_t)stream;
+    if (q.data && k.data && q.dtype == k.dtype)  // both in one launch
+        return device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, q, &k, s), "rope kernel (q, k)");
     if (q.data) {
-        if ((st = device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, q, s), "rope kernel (q)")))
+        if ((st = device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, q, nullptr, s),
+                                "rope kernel (q)")))
             return st;
     }
-    if (k.data) return device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, k, s), "rope kernel (k)");
+    if (k.data)
+        return device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, k, nullptr, s), "rope kernel (k)");
     return ok();
 }
 

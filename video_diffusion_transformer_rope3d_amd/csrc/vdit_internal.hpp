@@ -200,8 +200,9 @@ struct RopeDev {
 
 hipError_t launch_positions(vdit_grid grid, int32_t t0, int32_t* out, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+// Rotates x0, and x1 (of the same dtype) in the same launch when it is not NULL.
 hipError_t launch_rope_inplace(const RopeDev& r, vdit_grid grid, int32_t t0, int32_t heads, int32_t head_dim,
-                               vdit_tensor x, hipStream_t s);
+                               vdit_tensor x0, const vdit_tensor* x1, hipStream_t s);
 hipError_t launch_kv_append(const vdit_kv_cache& c, const RopeDev* r, vdit_grid grid, int32_t t0, vdit_tensor k,
                             vdit_tensor v, hipStream_t s);
 hipError_t launch_plan_build(const PlanGeom& g, const int32_t* slot_frame_dev, int32_t n_qtiles, int32_t* plan,

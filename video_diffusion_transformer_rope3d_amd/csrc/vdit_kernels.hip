@@ -53,20 +53,24 @@ __device__ inline void store8(void* base, int64_t off, const float x[8]) {
     }
 }
 
-// ---- RoPE3D in place: one thread per (token, head, 8-channel chunk).
+// ---- RoPE3D in place: one thread per (token, head, 8-channel chunk) of tokens
+// [tok0, tok0 + n) of x0, and of x1 in the grid's second row when the call rotates two
+// tensors (Q and K in one launch).  The host keeps n * heads * chunks below 2^31, so the index
+// arithmetic is 32-bit.
 template <bool F32>
-__global__ void rope_inplace_kernel(RopeDev r, int32_t n, int32_t hw, int32_t width, int32_t t0, int32_t heads,
-                                    int32_t head_dim, void* x, int64_t st, int64_t sh) {
-    int32_t chunks = head_dim / 8;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)n * heads * chunks) return;
-    int32_t c = (int32_t)(i % chunks);
-    int64_t th = i / chunks;
-    int32_t h = (int32_t)(th % heads);
-    int32_t tok = (int32_t)(th / heads);
-    int32_t s = tok % hw;
-    int32_t pos_t = t0 + tok / hw, pos_h = s / width, pos_w = s % width;
-    int64_t off = (int64_t)tok * st + (int64_t)h * sh + c * 8;
+__global__ void rope_inplace_kernel(RopeDev r, int32_t tok0, int32_t n, int32_t hw, int32_t width, int32_t t0,
+                                    int32_t heads, int32_t head_dim, void* x0, int64_t st0, int64_t sh0, void* x1,
+                                    int64_t st1, int64_t sh1) {
+    const int32_t chunks = head_dim / 8, per_tok = heads * chunks;
+    const int32_t i = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= n * per_tok) return;
+    const int32_t lt = i / per_tok, rem = i - lt * per_tok;
+    const int32_t h = rem / chunks, c = rem - h * chunks;
+    const int32_t tok = tok0 + lt, s = tok % hw;
+    const int32_t pos_t = t0 + tok / hw, pos_h = s / width, pos_w = s % width;
+    const bool second = blockIdx.y != 0;
+    void* x = second ? x1 : x0;
+    const int64_t off = (int64_t)tok * (second ? st1 : st0) + (int64_t)h * (second ? sh1 : sh0) + c * 8;
     float v[8];
     load8<F32>(x, off, v);
     rope_rotate8(r, c * 4, pos_t, pos_h, pos_w, v);
@@ -402,17 +406,27 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s) 
 }
 
 hipError_t launch_rope_inplace(const RopeDev& r, vdit_grid grid, int32_t t0, int32_t heads, int32_t head_dim,
-                               vdit_tensor x, hipStream_t s) {
-    int32_t hw = grid.height * grid.width, n = grid.frames * hw;
-    int64_t total = (int64_t)n * heads * (head_dim / 8);
-    unsigned blocks = (unsigned)((total + kThreads - 1) / kThreads);
-    if (x.dtype == VDIT_DTYPE_FP32)
-        rope_inplace_kernel<true><<<blocks, kThreads, 0, s>>>(r, n, hw, grid.width, t0, heads, head_dim, x.data,
-                                                              x.stride_token, x.stride_head);
-    else
-        rope_inplace_kernel<false><<<blocks, kThreads, 0, s>>>(r, n, hw, grid.width, t0, heads, head_dim, x.data,
-                                                               x.stride_token, x.stride_head);
-    return hipGetLastError();
+                               vdit_tensor x0, const vdit_tensor* x1, hipStream_t s) {
+    const int32_t hw = grid.height * grid.width, n = grid.frames * hw;
+    const int64_t per_tok = (int64_t)heads * (head_dim / 8);
+    // token ranges of fewer than 2^31 threads per tensor
+    const int32_t step = (int32_t)std::min<int64_t>(n, (((int64_t)1 << 31) - kThreads) / per_tok);
+    const vdit_tensor y = x1 ? *x1 : x0;
+    for (int32_t tok0 = 0; tok0 < n; tok0 += step) {
+        const int32_t cnt = std::min(step, n - tok0);
+        const dim3 blocks((unsigned)((cnt * per_tok + kThreads - 1) / kThreads), x1 ? 2 : 1);
+        if (x0.dtype == VDIT_DTYPE_FP32)
+            rope_inplace_kernel<true><<<blocks, kThreads, 0, s>>>(r, tok0, cnt, hw, grid.width, t0, heads, head_dim,
+                                                                  x0.data, x0.stride_token, x0.stride_head, y.data,
+                                                                  y.stride_token, y.stride_head);
+        else
+            rope_inplace_kernel<false><<<blocks, kThreads, 0, s>>>(r, tok0, cnt, hw, grid.width, t0, heads, head_dim,
+                                                                   x0.data, x0.stride_token, x0.stride_head, y.data,
+                                                                   y.stride_token, y.stride_head);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D, bool F32>
