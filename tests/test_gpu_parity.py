@@ -235,6 +235,39 @@ def test_rope_q_and_k_in_one_call(qdt, kdt):
     assert np.array_equal(wide[:, heads:].float().cpu().numpy(), rest0)  # the other heads untouched
 
 
+@pytest.mark.parametrize("same", [False, True])
+def test_rope_q_and_k_sharing_memory(same):
+    """Q and K whose address ranges overlap take one launch after the other: the two head
+    halves of one buffer (disjoint elements) are each rotated once, and Q and K given as the
+    same tensor are rotated twice, in order, as two calls would."""
+    rng = np.random.default_rng(12)
+    fr, hgt, wid, t0, heads = 2, 5, 8, 4, 2
+    n = fr * hgt * wid
+    buf = to_dev(rng.standard_normal((n, 2 * heads, 64)).astype(np.float32), torch.bfloat16)
+    start = buf.float().cpu().numpy().astype(np.float64)
+    rope = B.Rope(64, (24, 20, 20), 1e4, 12, hgt, wid)
+    pos = oracle.token_positions(fr, hgt, wid, t0)
+    if same:
+        x = buf[:, :heads]
+        B.vdit_rope3d_qk(rope, B.grid(fr, hgt, wid), t0, heads, q=x, k=x)
+        once = oracle.rope3d(start[:, :heads], pos, (24, 20, 20), 1e4)
+        # the second rotation starts from the first one's bf16 result, as two calls would
+        mid = torch.from_numpy(once).to(torch.bfloat16).float().numpy().astype(np.float64)
+        ref = oracle.rope3d(mid, pos, (24, 20, 20), 1e4)
+        got = buf[:, :heads].float().cpu().numpy()
+        # each rounding errs by at most 2^-9 of its value and a rotation keeps a pair's norm,
+        # so two roundings stay within 2^-8 of the pair's norm per element (2^-7 with margin)
+        pair = np.repeat(np.linalg.norm(ref.reshape(n, heads, 32, 2), axis=3), 2, axis=2)
+        assert (np.abs(got - ref) <= pair * 2.0 ** -7 + 1e-6).all()
+        assert np.array_equal(buf[:, heads:].float().cpu().numpy(), start[:, heads:])
+    else:
+        B.vdit_rope3d_qk(rope, B.grid(fr, hgt, wid), t0, heads, q=buf[:, :heads], k=buf[:, heads:])
+        ref = np.concatenate([oracle.rope3d(start[:, :heads], pos, (24, 20, 20), 1e4),
+                              oracle.rope3d(start[:, heads:], pos, (24, 20, 20), 1e4)], axis=1)
+        got = buf.float().cpu().numpy()
+        assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
+
+
 @pytest.mark.parametrize("name", ["tiny", "small_chunk_pad"])
 def test_kv_append_cache_contents(name):
     w = get_workload(name)

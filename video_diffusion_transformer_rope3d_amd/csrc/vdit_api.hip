@@ -268,7 +268,15 @@ int vdit_rope3d_qk(const vdit_rope_cfg* cfg, vdit_grid grid, int32_t t0, int32_t
     if (n == 0) return ok();
     RopeDev r = rope_dev(cfg);
     hipStream_t s = (hipStream_t)stream;
-    if (q.data && k.data && q.dtype == k.dtype)  // both in one launch
+    // Q and K in one launch when they have one dtype and their address ranges are disjoint;
+    // otherwise one launch after the other, so that elements they share are rotated in order.
+    auto range_end = [&](const vdit_tensor& x) {
+        const int64_t es = x.dtype == VDIT_DTYPE_FP32 ? 4 : 2;
+        return (uintptr_t)x.data + (uintptr_t)(((int64_t)(n - 1) * x.stride_token + (int64_t)(heads - 1) * x.stride_head +
+                                                cfg->head_dim) * es);
+    };
+    if (q.data && k.data && q.dtype == k.dtype &&
+        (range_end(q) <= (uintptr_t)k.data || range_end(k) <= (uintptr_t)q.data))
         return device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, q, &k, s), "rope kernel (q, k)");
     if (q.data) {
         if ((st = device_status(launch_rope_inplace(r, grid, t0, heads, cfg->head_dim, q, nullptr, s),
