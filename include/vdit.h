@@ -162,8 +162,10 @@ int vdit_rope_table_build(const vdit_rope_cfg* cfg, float* host_out, size_t cap_
  * for time and the two spatial axes) with the global time index above.
  * Rotates q and/or k ([frames*height*width][heads][head_dim], bf16 or fp32, device) in
  * place at positions (t0 + f, h, w); fp32 arithmetic, one rounding to the tensor's
- * dtype.  A tensor with data == NULL is skipped.  Errors: coordinates beyond the table
- * rows, head_dim not 64 or 128, bad strides -> INVALID_ARG / UNSUPPORTED. */
+ * dtype.  A tensor with data == NULL is skipped.  q and k of one dtype whose address
+ * ranges are disjoint are rotated in one launch; otherwise q is rotated first, then k (an
+ * element that both hold is rotated twice).  Errors: coordinates beyond the table rows,
+ * head_dim not 64 or 128, bad strides -> INVALID_ARG / UNSUPPORTED. */
 int vdit_rope3d_qk(const vdit_rope_cfg* cfg, vdit_grid grid, int32_t t0, int32_t heads,
                    vdit_tensor q, vdit_tensor k, void* stream);
 
