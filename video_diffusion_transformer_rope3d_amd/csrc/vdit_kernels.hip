@@ -288,8 +288,19 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(RopeDev r, bool has
     constexpr int PITCH = AppendLds<D>::PITCH;
     constexpr int VT_ITEMS = D * (kAppendTok / 8) / kThreads;  // (channel, 8-key group) items per thread
     __shared__ std::conditional_t<PLAN, AppendPlanLds<D>, AppendLds<D>> lds;
-    const int32_t h = blockIdx.y;
-    int32_t bx = blockIdx.x;
+    // Workgroups are dispatched round-robin over the 8 XCDs; each XCD takes a contiguous range
+    // of (head, token block) pairs instead, so neighbouring token blocks of a head, which share
+    // the 128-byte lines at the ends of their V^T row pieces (a frame's keys start at
+    // slot * frame_stride, not on a line), write them into one L2.
+    int32_t h, bx;
+    {
+        constexpr int kXcd = 8;
+        const int total = (int)(gridDim.x * gridDim.y), lin = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        const int q = total / kXcd, r = total % kXcd, xcd = lin % kXcd, idx = lin / kXcd;
+        const int item = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+        h = item / (int)gridDim.x;
+        bx = item % (int)gridDim.x;
+    }
     if constexpr (PLAN) {
         if (bx == 0) {
             if (h == 0) plan_build_block(ap.g, slot_frame, t0, frames, ap.nq, ap.plan, lds.plan);
