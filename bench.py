@@ -470,15 +470,16 @@ def measure(args, name, steps, warmup, cold_steps, tau=None, separate_plan=False
         step()
     torch.cuda.synchronize()
     words = plan.cpu().numpy()
-    header = words[:8]
+    hw = B.PLAN_HEADER_WORDS
+    header = words[:hw]
     pairs = int(np.uint32(header[6])) + (int(np.uint32(header[7])) << 32)
     flop = 4.0 * w.head_dim * w.heads * pairs
     # work the kernels execute: a query tile's rows in whole 32-row waves (a wave past the
     # tile's end does no math), every span in whole 64-key tiles
     nq = int(header[4])
-    q_lens = words[8:8 + 2 * nq].reshape(-1, 2)[:, 1]
-    row_ptr = words[8 + 2 * nq:8 + 3 * nq + 1]
-    spans = words[8 + 3 * nq + 1:8 + 3 * nq + 1 + 2 * int(header[5])].reshape(-1, 2)
+    q_lens = words[hw:hw + 2 * nq].reshape(-1, 2)[:, 1]
+    row_ptr = words[hw + 2 * nq:hw + 3 * nq + 1]
+    spans = words[hw + 3 * nq + 1:hw + 3 * nq + 1 + 2 * int(header[5])].reshape(-1, 2)
     executed_pairs = sum(int((q_lens[i] + 31) // 32 * 32) * int(((spans[row_ptr[i]:row_ptr[i + 1], 1] + 63) // 64).sum())
                          * 64 for i in range(nq))
     executed_flop = 4.0 * w.head_dim * w.heads * executed_pairs

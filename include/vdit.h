@@ -66,8 +66,8 @@ extern "C" {
 
 /* plan word layout (int32): header, then query tiles, row pointers and spans */
 #define VDIT_PLAN_MAGIC 0x54494456 /* 'V' 'D' 'I' 'T' */
-#define VDIT_PLAN_VERSION 1
-#define VDIT_PLAN_HEADER_WORDS 8
+#define VDIT_PLAN_VERSION 2
+#define VDIT_PLAN_HEADER_WORDS 12
 
 typedef struct {
     void* data;           /* device */
@@ -199,9 +199,11 @@ int vdit_kv_append(vdit_kv_cache* cache, const vdit_rope_cfg* rope, vdit_grid gr
  * CHUNK_CAUSAL, one frame for LOG_RADIAL), so that all rows of a tile see the same keys.
  * For every tile the plan lists the maximal ascending runs ("spans") of visible physical
  * key indices of the cache's occupied slots.
- * Words (int32): header[8] = {VDIT_PLAN_MAGIC, VDIT_PLAN_VERSION, kind, tile, n_qtiles,
- * n_spans, pairs_lo, pairs_hi} where pairs = sum over tiles of q_len * (sum of span
- * lengths); then {q_start, q_len}[n_qtiles]; row_ptr[n_qtiles + 1]; {k_start, k_len}[n_spans].
+ * Words (int32): header[12] = {VDIT_PLAN_MAGIC, VDIT_PLAN_VERSION, kind, tile, n_qtiles,
+ * n_spans, pairs_lo, pairs_hi, q_t0, q_frames, tokens per frame, 0} where pairs = sum over
+ * tiles of q_len * (sum of span lengths) and q_t0, q_frames and the tokens per frame are the
+ * query call the plan was built for (vdit_block_attn_fwd rejects it for another call); then
+ * {q_start, q_len}[n_qtiles]; row_ptr[n_qtiles + 1]; {k_start, k_len}[n_spans].
  * vdit_plan_qtiles: number of query tiles (depends on the rule and grid only).
  * vdit_plan_bound: upper bound on the plan size in words for this cache.
  * vdit_plan_mask: where = VDIT_WHERE_HOST reads slot_frame_host and writes host memory

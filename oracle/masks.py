@@ -33,7 +33,7 @@ from fractions import Fraction
 import numpy as np
 
 PLAN_MAGIC = 0x54494456  # bytes 'V','D','I','T' little-endian
-PLAN_VERSION = 1
+PLAN_VERSION = 2
 KIND_CODE = {"dense": 0, "chunk_causal": 1, "log_radial": 2, "log_radial_causal": 3}
 
 
@@ -129,18 +129,19 @@ def plan_from_mask(mask, q_t, q_s, qtiles, k_phys, k_t, k_s):
     return spans_per_tile
 
 
-def serialize_plan(mask, qtiles, spans_per_tile) -> np.ndarray:
-    """Plan as int32 words: header[8], qtile{start,len}[n], row_ptr[n+1], span{start,len}[m].
+def serialize_plan(mask, qtiles, spans_per_tile, q_t0: int, q_frames: int, tokens_per_frame: int) -> np.ndarray:
+    """Plan as int32 words: header[12], qtile{start,len}[n], row_ptr[n+1], span{start,len}[m].
 
-    header = magic, version, kind code, tile, n_qtiles, n_spans, flops_lo, flops_hi with
-    flops = sum over tiles and spans of q_len * k_len (the number of visible
-    query-key pairs), split into low and high 32-bit words.
+    header = magic, version, kind code, tile, n_qtiles, n_spans, flops_lo, flops_hi, q_t0,
+    q_frames, tokens_per_frame, 0 with flops = sum over tiles and spans of q_len * k_len (the
+    number of visible query-key pairs), split into low and high 32-bit words; the next three
+    words name the query call the plan was built for.
     """
     nq = len(qtiles)
     ns = sum(len(s) for s in spans_per_tile)
     pairs = sum(ql * sum(kl for _, kl in sp) for (_, ql), sp in zip(qtiles, spans_per_tile))
     words = [PLAN_MAGIC, PLAN_VERSION, KIND_CODE[mask.kind], mask.tile, nq, ns,
-             pairs & 0xFFFFFFFF, pairs >> 32]
+             pairs & 0xFFFFFFFF, pairs >> 32, q_t0, q_frames, tokens_per_frame, 0]
     for q0, ql in qtiles:
         words += [q0, ql]
     acc = 0

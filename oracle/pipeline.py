@@ -76,4 +76,4 @@ def plan_for(st) -> np.ndarray:
     w = st.w
     tiles = query_tiles(w.mask, w.q_frames, w.tokens_per_frame, w.q_t0)
     spans = plan_from_mask(w.mask, st.q_pos[:, 0], q_within_frame(st), tiles, st.k_phys, st.k_t, st.k_s)
-    return serialize_plan(w.mask, tiles, spans)
+    return serialize_plan(w.mask, tiles, spans, w.q_t0, w.q_frames, w.tokens_per_frame)

@@ -53,7 +53,7 @@ def run_workload(w, inputs, with_lse=True, rotate_q=True, q_override=None, works
 def device_plan_words(plan_dev):
     p = plan_dev.cpu().numpy()
     nq, ns = int(p[4]), int(p[5])
-    return p[:8 + 3 * nq + 1 + 2 * ns]
+    return p[:B.PLAN_HEADER_WORDS + 3 * nq + 1 + 2 * ns]
 
 
 def sample_rows(w, n_random=96, seed=0):

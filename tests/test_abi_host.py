@@ -155,7 +155,7 @@ def test_plan_errors(L):
     m = B.mask_cfg("chunk_causal", 1)
     assert L.vdit_plan_mask(ctypes.byref(m), g, 5, ctypes.byref(desc), B.VDIT_WHERE_HOST, buf.ctypes.data, buf.size,
                             ctypes.byref(used), None) == B.VDIT_ERR_BUFFER_TOO_SMALL
-    assert used.value == 8 + 3 * 3 + 1 + 2 * 4  # exact size is reported
+    assert used.value == 12 + 3 * 3 + 1 + 2 * 4  # exact size is reported
     assert (buf == 0).all()  # nothing written
     big = np.zeros(256, np.int32)
     for bad_mask, code in [(B.mask_cfg("chunk_causal", 0), B.VDIT_ERR_INVALID_ARG),
@@ -346,7 +346,7 @@ def test_dynamic_plan_errors(L):
     words = ctypes.c_size_t(0)
     assert L.vdit_plan_dynamic_bound(ctypes.byref(m), g, 0, ctypes.byref(desc), ctypes.byref(words)) == 0
     nq, nk = 3, 3  # one 24-token tile per frame; 3 slots of one key tile each
-    assert words.value == 8 + 2 * nq + nq + 1 + 2 * nq * nk
+    assert words.value == 12 + 2 * nq + nq + 1 + 2 * nq * nk
     for tau in (-0.1, 1.5, float("nan")):
         dyn = B.VditDynamicCfg(tau, 0.0)
         assert L.vdit_plan_dynamic(ctypes.byref(m), ctypes.byref(dyn), t, None, g, 0, ctypes.byref(desc), fake,

@@ -493,10 +493,12 @@ def test_split_stream_path_is_taken():
                                               ("small_chunk_pad", "span", False), ("small_chunk_pad", "kind", False),
                                               ("small_radial", "magic", False), ("small_radial", "span", False),
                                               ("small_radial", "tile", False), ("small_chunk_pad", "magic", True),
-                                              ("small_chunk_pad", "span", True), ("small_chunk_pad", "kind", True)])
+                                              ("small_chunk_pad", "span", True), ("small_chunk_pad", "kind", True),
+                                              ("small_chunk_pad", "t0", False), ("small_chunk_pad", "frames", False),
+                                              ("small_radial", "t0", False), ("small_chunk_pad", "t0", True)])
 def test_rejected_plan_gives_nan_outputs(name, corrupt, dyn):
     """A plan that does not belong to the call (wrong magic, another rule or tile size, another tile
-    count, a span past the cache) is not computed.  The check is in the kernel, which exits normally, so the call returns
+    count, another query start frame or frame count, a span past the cache) is not computed.  The check is in the kernel, which exits normally, so the call returns
     OK; the outputs it did not compute are NaN.  A bad header, or a bad span under the unit
     kernel (every workgroup validates the whole plan), poisons every output; under the tile
     kernel a bad span poisons its own query tile, here tile 0 of every head.  With the dynamic
@@ -518,14 +520,18 @@ def test_rejected_plan_gives_nan_outputs(name, corrupt, dyn):
         bad[2] = int(r["plan"][2].item()) if dyn else int(r["plan"][2].item()) ^ 1
     elif corrupt == "tile":
         bad[3] = int(bad[3].item()) // 2
+    elif corrupt == "t0":  # a plan built for the call one frame later
+        bad[8] = int(bad[8].item()) + 1
+    elif corrupt == "frames":  # for a call of one frame more (same tiles and spans otherwise)
+        bad[9] = int(bad[9].item()) + 1
     else:  # the first span of tile 0 starts at the end of the cache (8-aligned, outside it)
-        bad[8 + 3 * nq + 1] = s.cache.kv_rows
+        bad[12 + 3 * nq + 1] = s.cache.kv_rows
     lse = torch.zeros((w.heads, w.n_q), dtype=torch.float32, device="cuda")
     o = s.attend(r["q"], w.q_frames, w.q_t0, bad, lse=lse, mask=B.dynamic_mask(s.mask) if dyn else None)
     torch.cuda.synchronize()
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     if corrupt == "span" and (w.mask.kind == "log_radial" or dyn):
-        q0, ql = (int(x) for x in r["plan"][8:10].tolist())
+        q0, ql = (int(x) for x in r["plan"][12:14].tolist())
         assert np.isnan(o[q0:q0 + ql]).all() and np.isnan(lse[:, q0:q0 + ql]).all()
         assert np.isfinite(o[q0 + ql:]).all()
     else:
@@ -543,14 +549,14 @@ def test_query_tile_without_keys(dyn):
     r = run_workload(w, inp)
     p = device_plan_words(r["plan"]).copy()
     nq, ns = int(p[4]), int(p[5])
-    qt = p[8:8 + 2 * nq].reshape(nq, 2)
-    rp = p[8 + 2 * nq:8 + 3 * nq + 1].copy()
-    sp = p[8 + 3 * nq + 1:].reshape(ns, 2)
+    qt = p[12:12 + 2 * nq].reshape(nq, 2)
+    rp = p[12 + 2 * nq:12 + 3 * nq + 1].copy()
+    sp = p[12 + 3 * nq + 1:].reshape(ns, 2)
     drop = 1
     keep = np.r_[0:rp[drop], rp[drop + 1]:ns]
     rp2 = rp.copy()
     rp2[drop + 1:] -= rp[drop + 1] - rp[drop]
-    hdr = p[:8].copy()
+    hdr = p[:12].copy()
     hdr[5] = len(keep)
     if dyn:  # the words a dynamic plan of the same rule would carry
         hdr[2] |= B.VDIT_MASK_FLAG_DYNAMIC

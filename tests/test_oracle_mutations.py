@@ -103,7 +103,9 @@ MUTATIONS = [
      "tiles.append((start + off, mask.tile))", "ragged last tile not shortened"),
     ("masks.py", "cut = np.flatnonzero(np.diff(vis) != 1) + 1", "cut = np.flatnonzero(np.diff(vis) > 8) + 1",
      "runs merged across small gaps"),
-    ("masks.py", "pairs & 0xFFFFFFFF, pairs >> 32]", "pairs & 0xFFFF, pairs >> 32]", "pair count truncated"),
+    ("masks.py", "pairs & 0xFFFFFFFF, pairs >> 32, q_t0", "pairs & 0xFFFF, pairs >> 32, q_t0", "pair count truncated"),
+    ("masks.py", "q_t0, q_frames, tokens_per_frame, 0]", "q_frames, q_t0, tokens_per_frame, 0]",
+     "call words of the header swapped"),
     ("masks.py", "        acc += len(sp)\n        words.append(acc)", "        words.append(acc)\n        acc += len(sp)",
      "row pointers shifted by one tile"),
     # dynamic-threshold plan

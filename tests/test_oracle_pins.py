@@ -233,9 +233,9 @@ def test_tiny_plan_golden():
     st = oracle.build_layout(w)
     plan = oracle.plan_for(st)
     nq, ns = plan[4], plan[5]
-    qt = plan[8:8 + 2 * nq].reshape(nq, 2)
-    rp = plan[8 + 2 * nq:8 + 3 * nq + 1]
-    sp = plan[8 + 3 * nq + 1:].reshape(ns, 2)
+    qt = plan[12:12 + 2 * nq].reshape(nq, 2)
+    rp = plan[12 + 2 * nq:12 + 3 * nq + 1]
+    sp = plan[12 + 3 * nq + 1:].reshape(ns, 2)
     rows = _read_golden("tiny_plan.txt")
     assert len(rows) == nq
     for i, line in enumerate(rows):
@@ -243,7 +243,8 @@ def test_tiny_plan_golden():
         assert [int(x) for x in head.split()] == qt[i].tolist()
         want = [tuple(int(x) for x in s.split()) for s in spans.split(",")]
         assert [tuple(x) for x in sp[rp[i]:rp[i + 1]].tolist()] == want
-    assert plan[0] == 0x54494456 and plan[1] == 1 and plan[3] == 128
+    assert plan[0] == 0x54494456 and plan[1] == 2 and plan[3] == 128
+    assert plan[8:12].tolist() == [5, 3, 24, 0]  # the call: frames 5..7 of 4 x 6 tokens
     pairs = int(plan[6]) + (int(plan[7]) << 32)
     assert pairs == 24 * 24 + 24 * 48 + 24 * 72
 
@@ -295,9 +296,9 @@ def test_plan_expands_to_element_mask(name):
     st = oracle.build_layout(w)
     plan = oracle.plan_for(st)
     nq, ns = plan[4], plan[5]
-    qt = plan[8:8 + 2 * nq].reshape(nq, 2)
-    rp = plan[8 + 2 * nq:8 + 3 * nq + 1]
-    sp = plan[8 + 3 * nq + 1:].reshape(ns, 2)
+    qt = plan[12:12 + 2 * nq].reshape(nq, 2)
+    rp = plan[12 + 2 * nq:12 + 3 * nq + 1]
+    sp = plan[12 + 3 * nq + 1:].reshape(ns, 2)
     assert qt[:, 1].sum() == w.n_q and (qt[:, 1] <= w.mask.tile).all()
     phys_to_key = {int(p): i for i, p in enumerate(st.k_phys)}
     s_q = np.arange(w.n_q) % w.tokens_per_frame
@@ -344,7 +345,8 @@ def test_padded_plan_golden():
             head, body = wt.split(":")
             assert [q0, ql] == [int(x) for x in head.split()]
             assert sp == [tuple(int(x) for x in s.split()) for s in body.split(",")]
-        words = serialize_plan(mask, qtiles, spans)
+        words = serialize_plan(mask, qtiles, spans, qt0, qf, 15)
+        assert words[8:12].tolist() == [qt0, qf, 15, 0]
         pairs = sum(ql * sum(kl for _, kl in sp) for (_, ql), sp in zip(qtiles, spans))
         assert int(np.uint32(words[6])) + (int(np.uint32(words[7])) << 32) == pairs
 
@@ -353,11 +355,12 @@ def test_plan_pair_count_words_beyond_32_bits():
     """Header words 6, 7 hold the visible-pair count q_len * sum(k_len) in two 32-bit halves."""
     from oracle.masks import serialize_plan
     mask = MaskSpec("dense")
-    words = serialize_plan(mask, [(0, 128)], [[(0, 40_000_000), (40_000_008, 5)]])
+    words = serialize_plan(mask, [(0, 128)], [[(0, 40_000_000), (40_000_008, 5)]], 0, 1, 128)
     pairs = 128 * (40_000_000 + 5)
     assert pairs > 2 ** 32
     assert int(np.uint32(words[6])) == pairs % 2 ** 32 and int(np.uint32(words[7])) == pairs // 2 ** 32
-    assert words[4] == 1 and words[5] == 2 and words[8:10].tolist() == [0, 128] and words[10:12].tolist() == [0, 2]
+    assert words[4] == 1 and words[5] == 2 and words[8:12].tolist() == [0, 1, 128, 0]
+    assert words[12:14].tolist() == [0, 128] and words[14:16].tolist() == [0, 2]
 
 
 def test_log_radial_own_frame_and_window_edge():

@@ -19,6 +19,7 @@ VDIT_MASK_DENSE, VDIT_MASK_CHUNK_CAUSAL, VDIT_MASK_LOG_RADIAL, VDIT_MASK_LOG_RAD
 VDIT_MASK_FLAG_DYNAMIC = 0x100
 VDIT_WHERE_HOST, VDIT_WHERE_DEVICE = 0, 1
 VDIT_PLAN_MAGIC = 0x54494456
+PLAN_HEADER_WORDS = 12  # VDIT_PLAN_HEADER_WORDS
 MASK_KINDS = {"dense": VDIT_MASK_DENSE, "chunk_causal": VDIT_MASK_CHUNK_CAUSAL, "log_radial": VDIT_MASK_LOG_RADIAL,
               "log_radial_causal": VDIT_MASK_LOG_RADIAL_CAUSAL}
 
@@ -418,11 +419,11 @@ def vdit_block_attn_fwd_static(q, rope, g: VditGrid, q_t0: int, cache: KVCache, 
 def plan_fields(plan):
     """Split plan words (numpy) into (header, qtiles [n,2], row_ptr [n+1], spans [m,2])."""
     p = np.asarray(plan)
-    nq, ns = int(p[4]), int(p[5])
-    qt = p[8:8 + 2 * nq].reshape(nq, 2)
-    rp = p[8 + 2 * nq:8 + 3 * nq + 1]
-    sp = p[8 + 3 * nq + 1:8 + 3 * nq + 1 + 2 * ns].reshape(ns, 2)
-    return p[:8], qt, rp, sp
+    nq, ns, hw = int(p[4]), int(p[5]), PLAN_HEADER_WORDS
+    qt = p[hw:hw + 2 * nq].reshape(nq, 2)
+    rp = p[hw + 2 * nq:hw + 3 * nq + 1]
+    sp = p[hw + 3 * nq + 1:hw + 3 * nq + 1 + 2 * ns].reshape(ns, 2)
+    return p[:hw], qt, rp, sp
 
 
 def vdit_block_rel_l1_workspace_bytes(n_blocks: int, block_elems: int) -> int:

@@ -419,6 +419,7 @@ int vdit_plan_mask(const vdit_mask_cfg* mask, vdit_grid q_grid, int32_t q_t0, co
     plan_out[5] = k;
     plan_out[6] = (int32_t)(uint32_t)((uint64_t)pairs & 0xFFFFFFFFu);
     plan_out[7] = (int32_t)(uint32_t)((uint64_t)pairs >> 32);
+    plan_set_call(plan_out, g);
     return ok();
 }
 

@@ -211,6 +211,11 @@ __device__ inline long long uniform64(long long x) {
 // L2 latency on the path to the next DMA.  The broadcast keeps the value in a scalar
 // register whatever load the compiler picks (no waterfall loops on buffer offsets).
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+// The plan was built for this query call: its start frame, frames and tokens per frame.
+__device__ inline bool plan_for_call(const int32_t* plan, const AttnArgs& a) {
+    return plan[8] == a.t0 && plan[10] == a.hw && (int64_t)plan[9] * plan[10] == a.n_tokens;
+}
+
 __device__ inline int plan_word(const int32_t* p) {
     return __builtin_amdgcn_readfirstlane(*(const const_i32_t*)p);
 }
@@ -1091,9 +1096,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 2) void attn_tile_kernel(AttnArgs 
 
     const int32_t* plan = a.plan;
     const int nq = plan[4];
-    // a plan that does not belong to this call (another magic, rule, tile size or tile count) is
-    // not read out of bounds: NaN outputs instead
-    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[2] != a.plan_kind || plan[3] != a.plan_tile || nq != a.n_qtiles) {
+    // a plan that does not belong to this call (another magic, rule, tile size, tile count or
+    // query call) is not read out of bounds: NaN outputs instead
+    if (plan[0] != (int32_t)VDIT_PLAN_MAGIC || plan[2] != a.plan_kind || plan[3] != a.plan_tile || nq != a.n_qtiles ||
+        !plan_for_call(plan, a)) {
         poison_share<D, OF32>(a, blockIdx.x, gridDim.x);
         return;
     }
@@ -1317,7 +1323,7 @@ __global__ __launch_bounds__(kUnitWaves * 64, 1) void attn_unit_kernel(AttnArgs 
     // tiles of a unit share every K/V tile.  Units are numbered per head in tile order.
     if (tid == 0) s_bad = 0;
     if (tid < 4) s_pos[tid] = 0;  // set by the share lookup below
-    int bad = 0;
+    int bad = tid == 0 && !plan_for_call(plan, a) ? 1 : 0;  // built for another query call
     for (int q = tid; q < nq; q += kThreads) {
         const int qs = qtiles[2 * q], ql = qtiles[2 * q + 1], b = row_ptr[q], e = row_ptr[q + 1];
         int n = 0, same = 0;

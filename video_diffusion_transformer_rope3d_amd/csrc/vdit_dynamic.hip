@@ -369,6 +369,7 @@ __global__ __launch_bounds__(kDynThreads) void dyn_write_kernel(PlanGeom g, cons
             plan[5] = total;
             plan[6] = (int32_t)(uint32_t)(tot & 0xFFFFFFFFull);
             plan[7] = (int32_t)(uint32_t)(tot >> 32);
+            plan_set_call(plan, g);
         }
     }
     for (int j = t; j < nk; j += kDynThreads) s_p[j] = prox[(size_t)i * nk + j];

@@ -25,6 +25,15 @@ struct PlanGeom {
     int32_t capacity, frame_stride;  // cache
 };
 
+// Header words 8..11 of a plan: the query call it was built for (global start frame, frames,
+// tokens per frame) and a reserved zero.  Attention on another call rejects the plan.
+__host__ __device__ inline void plan_set_call(int32_t* plan, const PlanGeom& g) {
+    plan[8] = g.t0;
+    plan[9] = g.frames;
+    plan[10] = g.hw;
+    plan[11] = 0;
+}
+
 __host__ __device__ inline int32_t frame_stride_of(int32_t tokens_per_frame) {
     return (tokens_per_frame + 7) / 8 * 8;
 }

@@ -235,6 +235,7 @@ __device__ void plan_build_block(const PlanGeom& g, int32_t* slot_frame, int32_t
         plan[5] = carry;
         plan[6] = (int32_t)(uint32_t)(tot & 0xFFFFFFFFull);
         plan[7] = (int32_t)(uint32_t)(tot >> 32);
+        plan_set_call(plan, g);
     }
 }
 
